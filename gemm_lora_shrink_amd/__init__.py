@@ -1,0 +1,225 @@
+"""Python binding of the MI355X multi-LoRA library (liblora_mi355x.so).
+
+Thin ctypes layer over the C ABI in include/lora.h: it turns torch tensors
+into pointers, sizes and strides and raises LoraError on a non-OK status.
+Every step of the computation runs in the library's HIP kernels; there is no
+Python or CPU fallback, and importing this package fails loudly if the
+library has not been built (python -m gemm_lora_shrink_amd.build).
+
+Entry points (same names as the C ABI):
+    build_segments(idx, S, mode="auto") -> segment record (int32 tensor)
+    shrink(x, A, seg, ...)               -> v  [n_slices, T, r_max] fp32
+    expand(v, B, y, seg, out_offsets, ...) (y updated in place)
+    apply(x, A, B, y, seg, out_offsets, ...) = shrink then expand
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblora_mi355x.so")
+
+LORA_OK = 0
+LORA_ERR_INVALID_ARG = 1
+LORA_ERR_UNSUPPORTED = 2
+LORA_ERR_INDEX = 3
+LORA_ERR_HIP = 4
+
+MODES = {"auto": 0, "bgmv": 1, "sgmv": 2}
+SEG_FIELDS = {"info": 0, "perm": 1, "seg_slot": 2, "seg_start": 3, "groups": 4, "tiles": 5}
+INFO_WORDS = 16
+MAX_SLICES = 8
+
+_DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class LoraError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, status, message):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m gemm_lora_shrink_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.lora_segments_bytes.argtypes = [i32, i32]
+    lib.lora_segments_bytes.restype = sz
+    lib.lora_segments_offset.argtypes = [i32, i32, ctypes.c_int]
+    lib.lora_segments_offset.restype = i64
+    lib.lora_sgmv_min_tokens.argtypes = []
+    lib.lora_sgmv_min_tokens.restype = i32
+    lib.lora_build_segments.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.lora_build_segments.restype = ctypes.c_int
+    lib.lora_shrink.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, i32, i32, vp, vp, vp,
+                                i32, vp, vp]
+    lib.lora_shrink.restype = ctypes.c_int
+    lib.lora_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, vp, vp, vp, i32, i32, vp, vp,
+                                i32, vp, i64, vp]
+    lib.lora_expand.restype = ctypes.c_int
+    lib.lora_status_string.argtypes = [ctypes.c_int]
+    lib.lora_status_string.restype = ctypes.c_char_p
+    lib.lora_last_error.argtypes = []
+    lib.lora_last_error.restype = ctypes.c_char_p
+    lib.lora_abi_version.argtypes = []
+    lib.lora_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _load()
+
+
+def _status_name(status):
+    try:
+        return _load().lora_status_string(status).decode()
+    except Exception:
+        return f"status {status}"
+
+
+def _check(status):
+    if status != LORA_OK:
+        raise LoraError(status, _load().lora_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise LoraError(LORA_ERR_INVALID_ARG, f"unsupported dtype {t.dtype}") from None
+
+
+def _rows(t, name):
+    """(rows, width, row stride) of a 2-D tensor with unit inner stride."""
+    if t.dim() == 2 and t.numel() == 0:
+        return t.size(0), t.size(1), max(t.size(1), 1)
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise LoraError(LORA_ERR_INVALID_ARG, f"{name} must be 2-D with contiguous rows")
+    return t.size(0), t.size(1), t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
+
+
+def segments_bytes(T, S):
+    return int(_load().lora_segments_bytes(T, S))
+
+
+def segments_offset(T, S, field):
+    return int(_load().lora_segments_offset(T, S, SEG_FIELDS[field]))
+
+
+def sgmv_min_tokens():
+    return int(_load().lora_sgmv_min_tokens())
+
+
+def alloc_segments(T, S, device):
+    n = segments_bytes(T, S)
+    if n == 0:
+        raise LoraError(LORA_ERR_INVALID_ARG, f"bad sizes T={T} S={S}")
+    return torch.empty(n // 4, dtype=torch.int32, device=device)
+
+
+def build_segments(idx, S, *, mode="auto", seg=None, info_host=None, stream=None):
+    """Group the batch's tokens by slot; returns the segment record tensor."""
+    if idx.dtype != torch.int32 or idx.dim() != 1 or not idx.is_contiguous():
+        raise LoraError(LORA_ERR_INVALID_ARG, "idx must be a contiguous 1-D int32 tensor")
+    T = idx.numel()
+    if seg is None:
+        seg = alloc_segments(T, S, idx.device)
+    st = _load().lora_build_segments(_ptr(idx), T, S, MODES[mode], _ptr(seg),
+                                     _ptr(info_host), _stream(stream, idx.device))
+    _check(st)
+    return seg
+
+
+def segments_view(seg, T, S):
+    """Views of the record's documented fields (device tensors)."""
+    o = {k: segments_offset(T, S, k) for k in SEG_FIELDS}
+    return dict(info=seg[:INFO_WORDS], perm=seg[o["perm"]:o["perm"] + T],
+                seg_slot=seg[o["seg_slot"]:o["seg_slot"] + S],
+                seg_start=seg[o["seg_start"]:o["seg_start"] + S + 1])
+
+
+def shrink(x, A, seg, *, scale=None, ranks=None, v=None, active=True, stream=None):
+    """v[i][t][k] = scale[s] * A_i[s][k] . x[t] for active tokens.
+
+    x: [T, >=D] (contiguous rows, any row stride); A: list of [S, r_max, D].
+    Returns v ([n_slices, T, r_max] float32; allocated if not given).
+    """
+    A = list(A)
+    if not A or len(A) > MAX_SLICES:
+        raise LoraError(LORA_ERR_INVALID_ARG if not A else LORA_ERR_UNSUPPORTED,
+                        f"need 1..{MAX_SLICES} slices")
+    S, r_max, D = A[0].shape
+    T, _, ldx = _rows(x, "x")
+    for a in A:
+        if a.shape != (S, r_max, D) or not a.is_contiguous() or a.dtype != x.dtype:
+            raise LoraError(LORA_ERR_INVALID_ARG, "A slices must share shape, dtype and be contiguous")
+    if v is None:
+        v = torch.empty((len(A), T, r_max), dtype=torch.float32, device=x.device)
+    if v.dtype != torch.float32 or not v.is_contiguous() or v.shape != (len(A), T, r_max):
+        raise LoraError(LORA_ERR_INVALID_ARG, "v must be contiguous float32 [n_slices, T, r_max]")
+    ptrs = (ctypes.c_void_p * len(A))(*[a.data_ptr() for a in A])
+    st = _load().lora_shrink(_dtype_code(x), _ptr(x), ldx, T, D, len(A), ptrs, S, r_max,
+                             _ptr(ranks), _ptr(scale), _ptr(seg), 1 if active else 0,
+                             _ptr(v), _stream(stream, x.device))
+    _check(st)
+    return v
+
+
+def expand(v, B, y, seg, out_offsets, *, ranks=None, active=True, v_slice_stride=None,
+           stream=None):
+    """y[t, off_i:off_i+out_i] += B_i[s] @ v[i][t] for active tokens (in place)."""
+    B = list(B)
+    if not B or len(B) > MAX_SLICES:
+        raise LoraError(LORA_ERR_INVALID_ARG if not B else LORA_ERR_UNSUPPORTED,
+                        f"need 1..{MAX_SLICES} slices")
+    S, _, r_max = B[0].shape
+    T, _, ldy = _rows(y, "y")
+    for b in B:
+        if b.shape[0] != S or b.shape[2] != r_max or not b.is_contiguous() or b.dtype != y.dtype:
+            raise LoraError(LORA_ERR_INVALID_ARG, "B slices must share S, r_max, dtype and be contiguous")
+    if v.dtype != torch.float32 or not v.is_contiguous():
+        raise LoraError(LORA_ERR_INVALID_ARG, "v must be contiguous float32")
+    if v_slice_stride is None:
+        v_slice_stride = T * r_max if v.dim() == 3 and v.size(0) > 1 else 0
+    n = len(B)
+    ptrs = (ctypes.c_void_p * n)(*[b.data_ptr() for b in B])
+    sizes = (ctypes.c_int64 * n)(*[b.shape[1] for b in B])
+    offs = (ctypes.c_int64 * n)(*[int(o) for o in out_offsets])
+    st = _load().lora_expand(_dtype_code(y), _ptr(v), v_slice_stride, T, n, ptrs, sizes, offs,
+                             S, r_max, _ptr(ranks), _ptr(seg), 1 if active else 0, _ptr(y), ldy,
+                             _stream(stream, y.device))
+    _check(st)
+    return y
+
+
+def apply(x, A, B, y, seg, out_offsets, *, scale=None, ranks=None, v=None, active=True,
+          stream=None):
+    """Shrink then expand; returns (v, y)."""
+    v = shrink(x, A, seg, scale=scale, ranks=ranks, v=v, active=active, stream=stream)
+    expand(v, B, y, seg, out_offsets, ranks=ranks, active=active, stream=stream)
+    return v, y

@@ -1,0 +1,231 @@
+// C ABI entry points: host-side argument checks, the no-op gate and dispatch.
+//
+// Every check runs before anything is enqueued, so a rejected call leaves
+// every buffer untouched.  The no-op gate follows "[LoRA] LoRA cuda graph
+// specialization" (Purpose, Implementation): whether any adapter is active is
+// a host-side fact, and when none is the call launches nothing at all; when
+// the call does run, the intermediate is cleared inside the shrink call.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+
+#define LORA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace lora {
+namespace {
+
+thread_local char g_err[512];
+
+lora_status fail(lora_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lora_status hip_fail(hipError_t e, const char* what) {
+  return fail(LORA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void clear_error() { g_err[0] = 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int vec_of(lora_dtype dt) { return dt == LORA_F32 ? 4 : 8; }
+
+bool valid_dtype(int dt) { return dt == LORA_F32 || dt == LORA_F16 || dt == LORA_BF16; }
+
+lora_status check_common(int dt, int32_t T, int32_t n_slices, int32_t S, int32_t r_max, const void* seg) {
+  if (!valid_dtype(dt)) return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", dt);
+  if (T < 0) return fail(LORA_ERR_INVALID_ARG, "T = %d is negative", T);
+  if (n_slices < 1) return fail(LORA_ERR_INVALID_ARG, "n_slices = %d must be >= 1", n_slices);
+  if (n_slices > LORA_MAX_SLICES)
+    return fail(LORA_ERR_UNSUPPORTED, "n_slices = %d exceeds %d", n_slices, LORA_MAX_SLICES);
+  if (S < 1) return fail(LORA_ERR_INVALID_ARG, "S = %d must be >= 1", S);
+  if (S > LORA_MAX_SLOTS) return fail(LORA_ERR_UNSUPPORTED, "S = %d exceeds %d", S, LORA_MAX_SLOTS);
+  if (r_max < 1) return fail(LORA_ERR_INVALID_ARG, "r_max = %d must be >= 1", r_max);
+  if (r_max > LORA_MAX_RANK) return fail(LORA_ERR_UNSUPPORTED, "r_max = %d exceeds %d", r_max, LORA_MAX_RANK);
+  if (r_max % vec_of((lora_dtype)dt))
+    return fail(LORA_ERR_UNSUPPORTED, "r_max = %d must be a multiple of %d for this dtype", r_max,
+                vec_of((lora_dtype)dt));
+  if (!seg) return fail(LORA_ERR_INVALID_ARG, "segment record is null");
+  if (reinterpret_cast<uintptr_t>(seg) & 255u)
+    return fail(LORA_ERR_INVALID_ARG, "segment record must be 256-byte aligned");
+  return LORA_OK;
+}
+
+}  // namespace
+}  // namespace lora
+
+using namespace lora;
+
+LORA_EXPORT int32_t lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+LORA_EXPORT const char* lora_status_string(lora_status s) {
+  switch (s) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_INVALID_ARG: return "LORA_ERR_INVALID_ARG";
+    case LORA_ERR_UNSUPPORTED: return "LORA_ERR_UNSUPPORTED";
+    case LORA_ERR_INDEX: return "LORA_ERR_INDEX";
+    case LORA_ERR_HIP: return "LORA_ERR_HIP";
+  }
+  return "LORA_ERR_UNKNOWN";
+}
+
+LORA_EXPORT const char* lora_last_error(void) { return g_err; }
+
+LORA_EXPORT int32_t lora_sgmv_min_tokens(void) { return kSgmvMinTokens; }
+
+LORA_EXPORT size_t lora_segments_bytes(int32_t T, int32_t S) {
+  if (T < 0 || S < 1 || S > LORA_MAX_SLOTS) return 0;
+  const SegLayout L = seg_layout(T, S);
+  return (size_t)(((L.words * 4) + 255) & ~int64_t(255));
+}
+
+LORA_EXPORT int64_t lora_segments_offset(int32_t T, int32_t S, lora_seg_field field) {
+  if (T < 0 || S < 1 || S > LORA_MAX_SLOTS) return -1;
+  const SegLayout L = seg_layout(T, S);
+  switch (field) {
+    case LORA_SEG_INFO: return 0;
+    case LORA_SEG_PERM: return L.perm;
+    case LORA_SEG_SLOT: return L.seg_slot;
+    case LORA_SEG_START: return L.seg_start;
+    case LORA_SEG_GROUPS: return L.groups;
+    case LORA_SEG_TILES: return L.tiles;
+  }
+  return -1;
+}
+
+LORA_EXPORT lora_status lora_build_segments(const int32_t* idx, int32_t T, int32_t S, int32_t mode, void* seg,
+                                            int32_t* info_host, hipStream_t stream) {
+  clear_error();
+  if (T < 0) return fail(LORA_ERR_INVALID_ARG, "T = %d is negative", T);
+  if (S < 1) return fail(LORA_ERR_INVALID_ARG, "S = %d must be >= 1", S);
+  if (S > LORA_MAX_SLOTS) return fail(LORA_ERR_UNSUPPORTED, "S = %d exceeds %d", S, LORA_MAX_SLOTS);
+  if (mode != LORA_MODE_AUTO && mode != LORA_MODE_BGMV && mode != LORA_MODE_SGMV)
+    return fail(LORA_ERR_INVALID_ARG, "unknown mode %d", mode);
+  if (!seg) return fail(LORA_ERR_INVALID_ARG, "segment record is null");
+  if (reinterpret_cast<uintptr_t>(seg) & 255u)
+    return fail(LORA_ERR_INVALID_ARG, "segment record must be 256-byte aligned");
+  if (T > 0 && !idx) return fail(LORA_ERR_INVALID_ARG, "idx is null");
+  hipError_t e = launch_build_segments(idx, T, S, mode, static_cast<int32_t*>(seg), stream);
+  if (e != hipSuccess) return hip_fail(e, "segment build launch");
+  if (info_host) {
+    e = hipMemcpyAsync(info_host, seg, kInfoWords * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "info copy");
+  }
+  return LORA_OK;
+}
+
+LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D,
+                                    int32_t n_slices, const void* const* A, int32_t S, int32_t r_max,
+                                    const int32_t* ranks, const float* scale, const void* seg,
+                                    int32_t active_hint, float* v, hipStream_t stream) {
+  clear_error();
+  lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
+  if (st != LORA_OK) return st;
+  const int vec = vec_of(dt);
+  if (D < 1) return fail(LORA_ERR_INVALID_ARG, "D = %d must be >= 1", D);
+  if (T == 0) return LORA_OK;  // empty batch: nothing to read or write
+  if (ldx < D) return fail(LORA_ERR_INVALID_ARG, "ldx = %lld is smaller than D = %d", (long long)ldx, D);
+  if (D % vec || ldx % vec)
+    return fail(LORA_ERR_UNSUPPORTED, "D and ldx must be multiples of %d elements for this dtype", vec);
+  if (!x || !v) return fail(LORA_ERR_INVALID_ARG, "x or v is null");
+  if (!aligned16(x) || !aligned16(v)) return fail(LORA_ERR_UNSUPPORTED, "x and v must be 16-byte aligned");
+  if (!A) return fail(LORA_ERR_INVALID_ARG, "A pointer array is null");
+  ShrinkParams p = {};
+  for (int i = 0; i < n_slices; ++i) {
+    if (!A[i]) return fail(LORA_ERR_INVALID_ARG, "A[%d] is null", i);
+    if (!aligned16(A[i])) return fail(LORA_ERR_UNSUPPORTED, "A[%d] must be 16-byte aligned", i);
+    p.A[i] = A[i];
+  }
+  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
+
+  p.x = x;
+  p.ldx = ldx;
+  p.ranks = ranks;
+  p.scale = scale;
+  p.rec = static_cast<const int32_t*>(seg);
+  p.v = v;
+  p.v_slice_stride = (int64_t)T * r_max;
+  p.D = D;
+  p.S = S;
+  p.r_max = r_max;
+  p.n_slices = n_slices;
+  p.T = T;
+
+  hipError_t e = launch_fill_zero(v, (int64_t)n_slices * T * r_max, stream);
+  if (e != hipSuccess) return hip_fail(e, "clear of v");
+  e = launch_bgmv_shrink(dt, p, /*tiles=*/false, stream);
+  if (e != hipSuccess) return hip_fail(e, "gather shrink launch");
+  if (dt == LORA_F32) e = launch_bgmv_shrink(dt, p, /*tiles=*/true, stream);
+  else e = launch_sgmv_shrink(dt, p, stream);
+  if (e != hipSuccess) return hip_fail(e, "segmented shrink launch");
+  return LORA_OK;
+}
+
+LORA_EXPORT lora_status lora_expand(lora_dtype dt, const float* v, int64_t v_slice_stride, int32_t T,
+                                    int32_t n_slices, const void* const* B, const int64_t* out_sizes,
+                                    const int64_t* out_offsets, int32_t S, int32_t r_max, const int32_t* ranks,
+                                    const void* seg, int32_t active_hint, void* y, int64_t ldy,
+                                    hipStream_t stream) {
+  clear_error();
+  lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
+  if (st != LORA_OK) return st;
+  const int vec = vec_of(dt);
+  if (T == 0) return LORA_OK;  // empty batch: nothing to read or write
+  if (!v || !y) return fail(LORA_ERR_INVALID_ARG, "v or y is null");
+  if (!aligned16(v) || !aligned16(y)) return fail(LORA_ERR_UNSUPPORTED, "v and y must be 16-byte aligned");
+  if (!B || !out_sizes || !out_offsets) return fail(LORA_ERR_INVALID_ARG, "B, out_sizes or out_offsets is null");
+  if (v_slice_stride < 0) return fail(LORA_ERR_INVALID_ARG, "v_slice_stride is negative");
+  if (v_slice_stride % 4) return fail(LORA_ERR_UNSUPPORTED, "v_slice_stride must be a multiple of 4 floats");
+  if (v_slice_stride != 0 && v_slice_stride < (int64_t)T * r_max)
+    return fail(LORA_ERR_INVALID_ARG, "v_slice_stride is smaller than T * r_max");
+  if (ldy < 1 || ldy % vec) return fail(LORA_ERR_UNSUPPORTED, "ldy must be a positive multiple of %d", vec);
+  ExpandParams p = {};
+  std::vector<std::pair<int64_t, int64_t>> cols;
+  for (int i = 0; i < n_slices; ++i) {
+    if (!B[i]) return fail(LORA_ERR_INVALID_ARG, "B[%d] is null", i);
+    if (!aligned16(B[i])) return fail(LORA_ERR_UNSUPPORTED, "B[%d] must be 16-byte aligned", i);
+    if (out_sizes[i] < 1) return fail(LORA_ERR_INVALID_ARG, "out_sizes[%d] must be >= 1", i);
+    if (out_offsets[i] < 0) return fail(LORA_ERR_INVALID_ARG, "out_offsets[%d] is negative", i);
+    if (out_sizes[i] % vec || out_offsets[i] % vec)
+      return fail(LORA_ERR_UNSUPPORTED, "out_sizes[%d] and out_offsets[%d] must be multiples of %d", i, i, vec);
+    if (out_offsets[i] + out_sizes[i] > ldy)
+      return fail(LORA_ERR_INVALID_ARG, "slice %d ends past ldy", i);
+    if (out_sizes[i] > (int64_t)1 << 30) return fail(LORA_ERR_UNSUPPORTED, "out_sizes[%d] too large", i);
+    p.B[i] = B[i];
+    p.out_size[i] = out_sizes[i];
+    p.out_off[i] = out_offsets[i];
+    cols.emplace_back(out_offsets[i], out_offsets[i] + out_sizes[i]);
+  }
+  std::sort(cols.begin(), cols.end());
+  for (size_t i = 1; i < cols.size(); ++i)
+    if (cols[i].first < cols[i - 1].second) return fail(LORA_ERR_INVALID_ARG, "output slices overlap");
+  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
+
+  p.v = v;
+  p.v_slice_stride = v_slice_stride;
+  p.ranks = ranks;
+  p.rec = static_cast<const int32_t*>(seg);
+  p.y = y;
+  p.ldy = ldy;
+  p.S = S;
+  p.r_max = r_max;
+  p.n_slices = n_slices;
+  p.T = T;
+
+  hipError_t e = launch_bgmv_expand(dt, p, /*tiles=*/false, stream);
+  if (e != hipSuccess) return hip_fail(e, "gather expand launch");
+  if (dt == LORA_F32) e = launch_bgmv_expand(dt, p, /*tiles=*/true, stream);
+  else e = launch_sgmv_expand(dt, p, stream);
+  if (e != hipSuccess) return hip_fail(e, "segmented expand launch");
+  return LORA_OK;
+}

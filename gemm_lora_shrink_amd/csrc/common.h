@@ -1,0 +1,226 @@
+// Internal definitions shared by the library's HIP sources: storage-type traits,
+// the segment-record layout and the parameter blocks passed to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lora.h"
+
+namespace lora {
+
+// ---------------------------------------------------------------------------
+// Work decomposition constants
+// ---------------------------------------------------------------------------
+constexpr int kInfoWords = 16;
+constexpr int kGroup = 16;  // tokens per gather (BGMV) work item
+constexpr int kTile = 64;   // tokens per segmented (SGMV) work item
+constexpr int kSgmvMinTokens = 48;  // AUTO: slots with this many tokens go to SGMV
+
+enum InfoWord {
+  kNumActive = 0,
+  kNumSegments = 1,
+  kMaxSegLen = 2,
+  kStatus = 3,
+  kNumGroups = 4,
+  kNumTiles = 5,
+  kBuiltT = 6,
+  kBuiltS = 7,
+};
+
+// One work item: tokens perm[p0 .. p0 + cnt) all have slot `slot`.
+struct Item {
+  int p0, cnt, slot, seg;
+};
+
+struct SegLayout {
+  int64_t perm, seg_slot, seg_start, groups, tiles, words;
+  int64_t cap_groups, cap_tiles;
+};
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__host__ __device__ inline SegLayout seg_layout(int64_t T, int64_t S) {
+  SegLayout L;
+  L.perm = kInfoWords;
+  L.seg_slot = L.perm + T;
+  L.seg_start = L.seg_slot + S;
+  L.groups = (L.seg_start + S + 1 + 3) & ~int64_t(3);  // 16-byte aligned items
+  int64_t minST = S < T ? S : T;
+  L.cap_groups = ceil_div(T, kGroup) + minST;
+  L.tiles = L.groups + 4 * L.cap_groups;
+  L.cap_tiles = ceil_div(T, kTile) + minST;
+  L.words = L.tiles + 4 * L.cap_tiles;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Storage types
+// ---------------------------------------------------------------------------
+typedef _Float16 half_t;
+typedef __bf16 bf16_t;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline float bf16_bits_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round-to-nearest-even conversions of one fp32 value to the 16-bit types,
+// returned as the 16-bit pattern.
+__device__ inline uint32_t float_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<bf16_t>(f));
+}
+__device__ inline uint32_t float_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<half_t>(f));
+}
+
+// Reinterpret one 32-bit word as two 16-bit lanes.  The word is always passed
+// by value: this compiler mis-lowers __builtin_bit_cast applied directly to an
+// element of an ext_vector (it reads element 0 whatever the index), so vector
+// elements are first copied into a scalar.
+__device__ inline f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ inline bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// Traits: Elem is the storage type; a "vec" is 16 bytes of it.
+template <typename Elem> struct Traits;
+
+template <> struct Traits<float> {
+  static constexpr int kVec = 4;  // elements per 16 bytes
+  static constexpr lora_dtype kDtype = LORA_F32;
+  // dot of two 16-byte vectors accumulated into acc (fp32 FMA)
+  __device__ static inline float dot(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ai = a[i], bi = b[i];
+      acc = __builtin_fmaf(__uint_as_float(ai), __uint_as_float(bi), acc);
+    }
+    return acc;
+  }
+  __device__ static inline void to_float(u32x4 a, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ai = a[i];
+      out[i] = __uint_as_float(ai);
+    }
+  }
+  __device__ static inline float elem_to_float(uint32_t bits) { return __uint_as_float(bits); }
+};
+
+template <> struct Traits<half_t> {
+  static constexpr int kVec = 8;
+  static constexpr lora_dtype kDtype = LORA_F16;
+  __device__ static inline float dot(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ai = a[i], bi = b[i];
+      acc = __builtin_amdgcn_fdot2(as_f16x2(ai), as_f16x2(bi), acc, false);
+    }
+    return acc;
+  }
+  __device__ static inline void to_float(u32x4 a, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ai = a[i];
+      const f16x2 h = as_f16x2(ai);
+      out[2 * i] = (float)h[0];
+      out[2 * i + 1] = (float)h[1];
+    }
+  }
+  __device__ static inline float elem_to_float(uint32_t bits) {
+    return (float)__builtin_bit_cast(half_t, (uint16_t)bits);
+  }
+};
+
+template <> struct Traits<bf16_t> {
+  static constexpr int kVec = 8;
+  static constexpr lora_dtype kDtype = LORA_BF16;
+  __device__ static inline float dot(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ai = a[i], bi = b[i];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ai), as_bf16x2(bi), acc, false);
+    }
+    return acc;
+  }
+  __device__ static inline void to_float(u32x4 a, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ai = a[i];
+      out[2 * i] = __uint_as_float(ai << 16);
+      out[2 * i + 1] = __uint_as_float(ai & 0xffff0000u);
+    }
+  }
+  __device__ static inline float elem_to_float(uint32_t bits) { return bf16_bits_to_float(bits); }
+};
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks
+// ---------------------------------------------------------------------------
+struct ShrinkParams {
+  const void* x;
+  int64_t ldx;
+  const void* A[LORA_MAX_SLICES];
+  const int32_t* ranks;  // nullable
+  const float* scale;    // nullable
+  const int32_t* rec;    // segment record
+  float* v;
+  int64_t v_slice_stride;  // floats between slices of v (= T * r_max)
+  int32_t D, S, r_max, n_slices, T;
+};
+
+struct ExpandParams {
+  const float* v;
+  int64_t v_slice_stride;  // 0: all slices share one v
+  const void* B[LORA_MAX_SLICES];
+  int64_t out_size[LORA_MAX_SLICES];
+  int64_t out_off[LORA_MAX_SLICES];
+  const int32_t* ranks;  // nullable
+  const int32_t* rec;
+  void* y;
+  int64_t ldy;
+  int32_t S, r_max, n_slices, T;
+};
+
+// Reads work item `item_id` of a record and checks it against the call's sizes.
+// Returns false (the workgroup then does nothing) when the item does not exist,
+// when the record was built for other sizes, or when its fields are out of
+// range, so a wrong record can never make a kernel touch memory outside the
+// caller's buffers.
+__device__ inline bool load_item(const int32_t* rec, int T, int S, bool tiles, int64_t item_id, Item& it) {
+  if (rec[kBuiltT] != T || rec[kBuiltS] != S) return false;
+  const int n_items = rec[tiles ? kNumTiles : kNumGroups];
+  if (item_id >= n_items) return false;
+  const SegLayout L = seg_layout(T, S);
+  if (n_items > (tiles ? L.cap_tiles : L.cap_groups)) return false;
+  it = reinterpret_cast<const Item*>(rec + (tiles ? L.tiles : L.groups))[item_id];
+  const int cap = tiles ? kTile : kGroup;
+  return it.slot >= 0 && it.slot < S && it.p0 >= 0 && it.cnt > 0 && it.cnt <= cap && it.p0 + it.cnt <= T;
+}
+
+// Token index stored at perm position `pos`, clamped into [0, T).
+__device__ inline int load_token(const int32_t* rec, int T, int64_t perm_off, int pos) {
+  const int t = rec[perm_off + pos];
+  return t < 0 ? 0 : (t >= T ? T - 1 : t);
+}
+
+__device__ inline int slot_rank(const int32_t* ranks, int s, int r_max) {
+  if (!ranks) return r_max;
+  int r = ranks[s];
+  return r < 0 ? 0 : (r > r_max ? r_max : r);
+}
+
+// Host-side launchers (defined in the .hip files).
+hipError_t launch_build_segments(const int32_t* idx, int32_t T, int32_t S, int32_t mode, int32_t* rec,
+                                 hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_bgmv_shrink(lora_dtype dt, const ShrinkParams& p, bool tiles, hipStream_t stream);
+hipError_t launch_bgmv_expand(lora_dtype dt, const ExpandParams& p, bool tiles, hipStream_t stream);
+hipError_t launch_sgmv_shrink(lora_dtype dt, const ShrinkParams& p, hipStream_t stream);
+hipError_t launch_sgmv_expand(lora_dtype dt, const ExpandParams& p, hipStream_t stream);
+
+}  // namespace lora

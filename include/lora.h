@@ -1,0 +1,220 @@
+/*
+ * lora.h -- C ABI of the MI355X (gfx950) multi-LoRA shrink/expand library.
+ *
+ * What the library computes.  A batch of T tokens carries one adapter slot per
+ * token, idx[t] in {-1, 0 .. S-1}.  For every token whose slot s >= 0 and every
+ * output slice i (fused projections such as q/k/v or gate/up):
+ *
+ *     v[i][t][k]            = scale[s] * sum_d A_i[s][k][d] * x[t][d]   (k < r_s)
+ *     y[t][off_i + j]      += sum_k B_i[s][j][k] * v[i][t][k]
+ *
+ * Tokens with idx = -1 are base-model-only and are left untouched.
+ *   - One batch mixes LoRA and base-only requests, and adapters of different
+ *     ranks up to 64 ("Add multi-LoRA support", Features and Limitations).
+ *   - The stacked adapter tensors keep the input dimension contiguous: A_i is
+ *     [S][r_max][D] and B_i is [S][out_i][r_max] ("[Hardware][TPU][V1] Better
+ *     tpu multilora compilation", the gather baseline in the review thread).
+ *   - The intermediate v is fp32, because a half-precision intermediate loses
+ *     accuracy ("Add multi-LoRA support", Limitations, on the SGMV kernel).
+ *   - v is cleared inside lora_shrink, and only when some token is active
+ *     ("[LoRA] LoRA cuda graph specialization", Implementation).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device memory unless marked [host].  The caller owns every
+ *     buffer; the library allocates nothing and keeps no per-call state.
+ *   - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t; NULL
+ *     means the legacy default stream).  No call synchronises the device,
+ *     except where an argument is documented to.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is enqueued and no buffer is written.  lora_last_error()
+ *     then returns a description (per thread).
+ *   - The library is re-entrant; calls on distinct streams may overlap.
+ *   - x, A, B and y of one call share one dtype (all adapters have one dtype,
+ *     "Add multi-LoRA support", Limitations).  Arithmetic is fp32 accumulation
+ *     of exact products; y is rounded once, to nearest even, into its dtype.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+
+/* Largest supported rank ("Add multi-LoRA support", Limitations). */
+#define LORA_MAX_RANK 64
+/* Most output slices one call may cover (fused QKV uses 3, gate/up 2). */
+#define LORA_MAX_SLICES 8
+/* Most adapter slots one batch may index. */
+#define LORA_MAX_SLOTS 1024
+
+typedef enum {
+  LORA_OK = 0,
+  LORA_ERR_INVALID_ARG = 1, /* a null pointer, a negative size, a bad stride */
+  LORA_ERR_UNSUPPORTED = 2, /* a valid request outside the documented limits */
+  LORA_ERR_INDEX = 3,       /* device-side: some idx outside [-1, S-1] */
+  LORA_ERR_HIP = 4          /* the HIP runtime refused a launch or copy */
+} lora_status;
+
+typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
+
+/* How lora_build_segments splits each slot's tokens into kernel work items.
+ *   AUTO: slots with at least lora_sgmv_min_tokens() tokens go to the segmented
+ *         MFMA path (SGMV) in tiles of 64 tokens; the rest go to the gather
+ *         path (BGMV) in groups of at most 16 tokens.  The gather kernel
+ *         suits decode-shaped batches and the segmented kernel prefill
+ *         ("Add multi-LoRA support", Limitations: the gather kernel is not
+ *         efficient for prefill).
+ *   BGMV: every slot in groups of at most 16 tokens.
+ *   SGMV: every slot in tiles of at most 64 tokens.
+ * fp32 data always runs on the gather kernels, whatever the mode. */
+typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode;
+
+/* ------------------------------------------------------------------------ */
+/* Segment record                                                           */
+/* ------------------------------------------------------------------------ */
+/*
+ * lora_build_segments groups the active tokens of a batch by slot, once per
+ * batch; every LoRA layer of that batch then reuses the record.  The token
+ * indices are built on the host and moved to the device once ("[Hardware]
+ * [TPU][V1] Better tpu multilora compilation", review of the token index
+ * buffer).
+ *
+ * The record is one caller-allocated device buffer of lora_segments_bytes(T, S)
+ * bytes, 256-byte aligned, laid out as int32 words:
+ *
+ *   words [0, 16)             info
+ *       info[0] num_active    tokens with a valid slot
+ *       info[1] num_segments  slots with at least one token
+ *       info[2] max_seg_len   largest token count of one slot (0 if none)
+ *       info[3] status        LORA_OK, or LORA_ERR_INDEX if some idx was
+ *                             outside [-1, S-1]; such tokens are treated as -1
+ *       info[4] n_groups      gather work items (see mode)
+ *       info[5] n_tiles       segmented work items
+ *       info[6] T, info[7] S  the sizes the record was built for
+ *       info[8..15]           zero
+ *   perm       [T]      at lora_segments_offset(T, S, LORA_SEG_PERM); the first
+ *                       num_active entries are the active tokens ordered by slot
+ *                       ascending, then token index ascending (stable)
+ *   seg_slot   [S]      at ..._SEG_SLOT; first num_segments entries: the
+ *                       non-empty slots, ascending
+ *   seg_start  [S + 1]  at ..._SEG_START; segment g is
+ *                       perm[seg_start[g] .. seg_start[g+1]); entry
+ *                       num_segments equals num_active
+ *   work items          internal to the library (unspecified contents)
+ *
+ * Entries past the counts are unspecified.  The record is bit-exact and
+ * deterministic for a given (idx, S, mode).
+ */
+typedef enum {
+  LORA_SEG_INFO = 0,
+  LORA_SEG_PERM = 1,
+  LORA_SEG_SLOT = 2,
+  LORA_SEG_START = 3,
+  LORA_SEG_GROUPS = 4,
+  LORA_SEG_TILES = 5
+} lora_seg_field;
+
+/* Bytes of the segment record for T tokens and S slots (0 on bad sizes). */
+size_t lora_segments_bytes(int32_t T, int32_t S);
+
+/* Offset in int32 words of a field of the record (-1 on bad arguments). */
+int64_t lora_segments_offset(int32_t T, int32_t S, lora_seg_field field);
+
+/* Smallest slot token count that AUTO mode sends to the segmented kernels. */
+int32_t lora_sgmv_min_tokens(void);
+
+/*
+ * Build the segment record of one batch.
+ *   idx        [T] int32 device; slot per token, -1 for base-only
+ *   T          0 <= T; T = 0 gives an empty record
+ *   S          1 <= S <= LORA_MAX_SLOTS
+ *   mode       a lora_mode
+ *   seg        device record of lora_segments_bytes(T, S) bytes, 256-B aligned
+ *   info_host  [host] nullable; pinned host memory of 16 int32.  When given, the
+ *              16 info words are copied there asynchronously on `stream`; they
+ *              are valid after the stream is synchronised.
+ * One single-workgroup kernel; nothing else runs.
+ */
+lora_status lora_build_segments(const int32_t *idx, int32_t T, int32_t S, int32_t mode,
+                                void *seg, int32_t *info_host, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Shrink and expand                                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * Common arguments:
+ *   dt          dtype of x, A, B and y
+ *   T           tokens in the batch (the same T the record was built for)
+ *   n_slices    1 .. LORA_MAX_SLICES
+ *   S, r_max    slots and padded rank of the stacked adapters; 1 <= r_max <=
+ *               LORA_MAX_RANK and r_max a multiple of 8 (fp16/bf16) or 4 (fp32)
+ *   ranks       [S] int32 device, nullable (= r_max for every slot); only rank
+ *               rows/columns k < ranks[s] take part; values are clamped to
+ *               [0, r_max]
+ *   seg         the record lora_build_segments wrote for this batch's idx
+ *   active_hint 0 when the caller knows that no token of the batch has a valid
+ *               slot: the call then returns LORA_OK having enqueued nothing, so
+ *               a base-only batch costs no kernel at all ("[LoRA] LoRA cuda
+ *               graph specialization", Purpose and Implementation: the host
+ *               picks the no-LoRA path).  Any other value: the kernels run and
+ *               read the record's counts on the device, so the result is right
+ *               whatever the batch holds.
+ * Widths and strides (D, ldx, out_i, off_i, ldy) must be multiples of 8
+ * elements for fp16/bf16 and of 4 for fp32, and every base pointer 16-byte
+ * aligned; otherwise LORA_ERR_UNSUPPORTED.
+ */
+
+/*
+ * Shrink: v[i][t][k] = scale[s] * sum_d A_i[s][k][d] * x[t][d].
+ *   x        [T][ldx] device, row-major, D <= ldx
+ *   A        [host] array of n_slices device pointers, each [S][r_max][D]
+ *   scale    [S] fp32 device, nullable (= 1.0)
+ *   v        [n_slices][T][r_max] fp32 device, written in full when the call
+ *            runs: rows of inactive tokens and columns k >= r_s are 0
+ */
+lora_status lora_shrink(lora_dtype dt, const void *x, int64_t ldx, int32_t T, int32_t D,
+                        int32_t n_slices, const void *const *A, int32_t S, int32_t r_max,
+                        const int32_t *ranks, const float *scale, const void *seg,
+                        int32_t active_hint, float *v, hipStream_t stream);
+
+/*
+ * Expand: y[t][off_i + j] += sum_{k < r_s} B_i[s][j][k] * v[i][t][k] for active t.
+ *   v              fp32 device; slice i starts at v + i * v_slice_stride, rows of
+ *                  r_max floats (v_slice_stride = 0 shares one v by all slices)
+ *   B              [host] array of n_slices device pointers, each [S][out_i][r_max]
+ *   out_sizes      [host] n_slices widths out_i >= 1
+ *   out_offsets    [host] n_slices column offsets; off_i + out_i <= ldy
+ *   y              [T][ldy] device, updated in place; rows of inactive tokens and
+ *                  columns outside the slices are not read or written
+ */
+lora_status lora_expand(lora_dtype dt, const float *v, int64_t v_slice_stride, int32_t T,
+                        int32_t n_slices, const void *const *B, const int64_t *out_sizes,
+                        const int64_t *out_offsets, int32_t S, int32_t r_max,
+                        const int32_t *ranks, const void *seg, int32_t active_hint, void *y,
+                        int64_t ldy, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Static name of a status code. */
+const char *lora_status_string(lora_status s);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char *lora_last_error(void);
+
+/* LORA_ABI_VERSION of the built library. */
+int32_t lora_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

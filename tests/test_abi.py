@@ -1,0 +1,166 @@
+"""CPU tests of the C ABI: the library loads, exports what include/lora.h
+declares, reports the documented record layout, and rejects bad arguments on
+the host before touching the GPU.  No compute call is made here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemm_lora_shrink_amd as glsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = glsa.lib()
+    names = declared_functions()
+    assert "lora_shrink" in names and "lora_expand" in names and "lora_build_segments" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in lora.h but not exported"
+
+
+def test_version_and_status_strings():
+    lib = glsa.lib()
+    assert lib.lora_abi_version() == 1
+    for code, name in [(0, b"LORA_OK"), (1, b"LORA_ERR_INVALID_ARG"), (2, b"LORA_ERR_UNSUPPORTED"),
+                       (3, b"LORA_ERR_INDEX"), (4, b"LORA_ERR_HIP")]:
+        assert lib.lora_status_string(code) == name
+
+
+@pytest.mark.parametrize("T,S", [(0, 1), (1, 1), (64, 4), (256, 8), (8192, 16), (1024, 32),
+                                 (4096, 128), (37, 1024)])
+def test_segment_record_layout(T, S):
+    nbytes = glsa.segments_bytes(T, S)
+    assert nbytes % 256 == 0 and nbytes > 0
+    off = {k: glsa.segments_offset(T, S, k) for k in glsa.SEG_FIELDS}
+    assert off["info"] == 0 and off["perm"] == 16
+    assert off["seg_slot"] == 16 + T and off["seg_start"] == 16 + T + S
+    assert off["groups"] >= off["seg_start"] + S + 1 and off["groups"] % 4 == 0
+    cap_groups = -(-T // 16) + min(S, T)
+    cap_tiles = -(-T // 64) + min(S, T)
+    assert off["tiles"] == off["groups"] + 4 * cap_groups
+    assert (off["tiles"] + 4 * cap_tiles) * 4 <= nbytes
+
+
+def test_bad_sizes_give_zero_bytes():
+    assert glsa.segments_bytes(-1, 4) == 0
+    assert glsa.segments_bytes(10, 0) == 0
+    assert glsa.segments_bytes(10, 1025) == 0
+    assert glsa.segments_offset(10, 0, "perm") == -1
+
+
+# --------------------------------------------------------------------------
+# Host-side validation: every call below is rejected before any HIP call.
+# --------------------------------------------------------------------------
+
+FAKE = 0x10000  # a 256-byte aligned, never dereferenced address
+
+
+def _shrink(**kw):
+    a = dict(dt=1, x=FAKE, ldx=64, T=8, D=64, n_slices=1, A=[FAKE], S=4, r_max=16,
+             ranks=None, scale=None, seg=FAKE, active=1, v=FAKE)
+    a.update(kw)
+    A = (ctypes.c_void_p * max(1, len(a["A"])))(*a["A"]) if a["A"] is not None else None
+    return glsa.lib().lora_shrink(a["dt"], a["x"], a["ldx"], a["T"], a["D"], a["n_slices"], A,
+                                  a["S"], a["r_max"], a["ranks"], a["scale"], a["seg"],
+                                  a["active"], a["v"], None)
+
+
+def _expand(**kw):
+    a = dict(dt=2, v=FAKE, vss=0, T=8, n_slices=1, B=[FAKE], sizes=[64], offs=[0], S=4,
+             r_max=16, ranks=None, seg=FAKE, active=1, y=FAKE, ldy=64)
+    a.update(kw)
+    n = max(1, len(a["B"]))
+    B = (ctypes.c_void_p * n)(*a["B"])
+    sizes = (ctypes.c_int64 * n)(*a["sizes"])
+    offs = (ctypes.c_int64 * n)(*a["offs"])
+    return glsa.lib().lora_expand(a["dt"], a["v"], a["vss"], a["T"], a["n_slices"], B, sizes,
+                                  offs, a["S"], a["r_max"], a["ranks"], a["seg"], a["active"],
+                                  a["y"], a["ldy"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), glsa.LORA_ERR_INVALID_ARG),
+    (dict(T=-1), glsa.LORA_ERR_INVALID_ARG),
+    (dict(D=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(ldx=32), glsa.LORA_ERR_INVALID_ARG),
+    (dict(x=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(v=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(seg=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(seg=FAKE + 64), glsa.LORA_ERR_INVALID_ARG),
+    (dict(A=[0]), glsa.LORA_ERR_INVALID_ARG),
+    (dict(n_slices=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(n_slices=9, A=[FAKE] * 9), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(S=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(S=1025), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(r_max=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(r_max=72), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(r_max=12), glsa.LORA_ERR_UNSUPPORTED),      # not a multiple of 8 for fp16
+    (dict(D=60, ldx=64), glsa.LORA_ERR_UNSUPPORTED),  # D not a multiple of 8
+    (dict(x=FAKE + 8), glsa.LORA_ERR_UNSUPPORTED),    # misaligned
+])
+def test_shrink_rejects_bad_arguments(kw, status):
+    assert _shrink(**kw) == status
+    assert glsa.lib().lora_last_error()  # a description is set
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=-1), glsa.LORA_ERR_INVALID_ARG),
+    (dict(y=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(vss=-4), glsa.LORA_ERR_INVALID_ARG),
+    (dict(vss=6), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(vss=64), glsa.LORA_ERR_INVALID_ARG),          # smaller than T * r_max
+    (dict(sizes=[0]), glsa.LORA_ERR_INVALID_ARG),
+    (dict(offs=[8]), glsa.LORA_ERR_INVALID_ARG),        # ends past ldy
+    (dict(sizes=[60], ldy=64), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(n_slices=2, B=[FAKE, FAKE], sizes=[32, 32], offs=[0, 16]), glsa.LORA_ERR_INVALID_ARG),
+    (dict(ldy=0), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(B=[FAKE + 4]), glsa.LORA_ERR_UNSUPPORTED),
+])
+def test_expand_rejects_bad_arguments(kw, status):
+    assert _expand(**kw) == status
+    assert glsa.lib().lora_last_error()
+
+
+def test_fp32_allows_rank_multiple_of_four_but_checks_it():
+    assert _shrink(dt=0, r_max=12, active=0) == glsa.LORA_OK
+    assert _shrink(dt=0, r_max=6, active=0) == glsa.LORA_ERR_UNSUPPORTED
+
+
+def test_inactive_batch_is_a_host_side_no_op():
+    """active_hint = 0 returns OK after validation without any HIP call (no GPU here)."""
+    assert _shrink(active=0) == glsa.LORA_OK
+    assert _expand(active=0) == glsa.LORA_OK
+    assert glsa.lib().lora_last_error() == b""
+    # still validated first
+    assert _shrink(active=0, D=0) == glsa.LORA_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op():
+    assert _shrink(T=0) == glsa.LORA_OK
+    assert _expand(T=0) == glsa.LORA_OK
+
+
+def test_build_segments_rejects_bad_arguments():
+    lib = glsa.lib()
+    assert lib.lora_build_segments(FAKE, -1, 4, 0, FAKE, None, None) == glsa.LORA_ERR_INVALID_ARG
+    assert lib.lora_build_segments(FAKE, 4, 0, 0, FAKE, None, None) == glsa.LORA_ERR_INVALID_ARG
+    assert lib.lora_build_segments(FAKE, 4, 2000, 0, FAKE, None, None) == glsa.LORA_ERR_UNSUPPORTED
+    assert lib.lora_build_segments(FAKE, 4, 4, 9, FAKE, None, None) == glsa.LORA_ERR_INVALID_ARG
+    assert lib.lora_build_segments(FAKE, 4, 4, 0, 0, None, None) == glsa.LORA_ERR_INVALID_ARG
+    assert lib.lora_build_segments(FAKE, 4, 4, 0, FAKE + 16, None, None) == glsa.LORA_ERR_INVALID_ARG
+    assert lib.lora_build_segments(0, 4, 4, 0, FAKE, None, None) == glsa.LORA_ERR_INVALID_ARG
+
+
+def test_python_binding_raises_lora_error():
+    err = glsa.LoraError(glsa.LORA_ERR_INDEX, "x")
+    assert err.status == 3 and "LORA_ERR_INDEX" in str(err)
