@@ -7,9 +7,11 @@
 // the call does run, the intermediate is cleared inside the shrink call.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -42,6 +44,17 @@ int vec_of(lora_dtype dt) { return dt == LORA_F32 ? 4 : 8; }
 
 bool valid_dtype(int dt) { return dt == LORA_F32 || dt == LORA_F16 || dt == LORA_BF16; }
 
+// Kernel used for the expand of gather (decode) groups of 16-bit data.  The
+// matrix-core kernel is the default; LORA_MI355X_GATHER_EXPAND=valu selects the
+// VALU gather kernel instead (kept for comparison measurements).
+bool gather_expand_on_valu() {
+  static const bool valu = [] {
+    const char* e = getenv("LORA_MI355X_GATHER_EXPAND");
+    return e && strcmp(e, "valu") == 0;
+  }();
+  return valu;
+}
+
 lora_status check_common(int dt, int32_t T, int32_t n_slices, int32_t S, int32_t r_max, const void* seg) {
   if (!valid_dtype(dt)) return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", dt);
   if (T < 0) return fail(LORA_ERR_INVALID_ARG, "T = %d is negative", T);
@@ -62,6 +75,39 @@ lora_status check_common(int dt, int32_t T, int32_t n_slices, int32_t S, int32_t
 }
 
 }  // namespace
+
+int persistent_grid(const void* kernel, int block, size_t dyn_lds, int64_t max_useful) {
+  // (device, kernel) -> workgroups resident at once, computed on first use
+  struct Entry {
+    int device;
+    const void* kernel;
+    int blocks;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int resident = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& e : cache)
+      if (e.device == dev && e.kernel == kernel) resident = e.blocks;
+  }
+  if (resident == 0) {
+    int occ = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, dyn_lds) != hipSuccess || occ < 1) occ = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    resident = occ * cus;
+    std::lock_guard<std::mutex> lock(mu);
+    cache.push_back(Entry{dev, kernel, resident});
+  }
+  int64_t g = resident;
+  const int64_t useful = ((max_useful > 0 ? max_useful : 1) + kXcds - 1) / kXcds * kXcds;
+  if (g > useful) g = useful;
+  g = (g + kXcds - 1) / kXcds * kXcds;
+  return (int)g;
+}
+
 }  // namespace lora
 
 using namespace lora;
@@ -222,10 +268,16 @@ LORA_EXPORT lora_status lora_expand(lora_dtype dt, const float* v, int64_t v_sli
   p.n_slices = n_slices;
   p.T = T;
 
-  hipError_t e = launch_bgmv_expand(dt, p, /*tiles=*/false, stream);
-  if (e != hipSuccess) return hip_fail(e, "gather expand launch");
-  if (dt == LORA_F32) e = launch_bgmv_expand(dt, p, /*tiles=*/true, stream);
-  else e = launch_sgmv_expand(dt, p, stream);
-  if (e != hipSuccess) return hip_fail(e, "segmented expand launch");
+  hipError_t e;
+  if (dt == LORA_F32) {
+    e = launch_bgmv_expand(dt, p, /*tiles=*/false, stream);
+    if (e == hipSuccess) e = launch_bgmv_expand(dt, p, /*tiles=*/true, stream);
+  } else if (gather_expand_on_valu()) {
+    e = launch_bgmv_expand(dt, p, /*tiles=*/false, stream);
+    if (e == hipSuccess) e = launch_mfma_expand(dt, p, /*groups=*/false, /*tiles=*/true, stream);
+  } else {
+    e = launch_mfma_expand(dt, p, /*groups=*/true, /*tiles=*/true, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "expand launch");
   return LORA_OK;
 }

@@ -31,6 +31,9 @@ constexpr int kWavesPerWG = kThreads / 64;
 constexpr int kRowsPerPass = 4;                       // rank rows per wave per pass
 constexpr int kItemsPerPass = kRowsPerPass * kGroup;  // 64 (rank, token) sums per pass
 constexpr int kXChunkBytes = 2048;                    // bytes of one x row staged per workgroup
+constexpr int kColsPerLane = 4;
+constexpr int kExpandCols = kThreads * kColsPerLane;  // 1024 output columns per workgroup
+constexpr int kKChunk = 8;                            // rank elements per B load step
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -61,7 +64,7 @@ __device__ inline float wave_transpose_reduce64(float (&vals)[64]) {
 }
 
 template <typename Elem>
-__global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(ShrinkParams p, int which_list, int sub_per_item,
+__global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(ShrinkParams p, int use_tiles, int nsplit,
                                                                int d_chunk, int atomic_out) {
   using Tr = Traits<Elem>;
   constexpr int kVec = Tr::kVec;
@@ -69,36 +72,63 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(ShrinkParams p, i
   __shared__ __attribute__((aligned(16))) Elem s_x[kGroup][kChunkElems];
   __shared__ int s_tok[kGroup];
 
+  // work list: (16-token unit, D split, slice), unit fastest, so that the
+  // groups of one slot (adjacent in the list) read the same A rows in one L2.
+  // A tile of 64 tokens is processed as four 16-token units.
   const SegLayout L = seg_layout(p.T, p.S);
-  const int item_id = blockIdx.x / sub_per_item;
-  Item it;
-  if (!load_item(p.rec, p.T, p.S, which_list != 0, item_id, it)) return;
-  const int sub = blockIdx.x - item_id * sub_per_item;
-  const int cnt = min(kGroup, it.cnt - sub * kGroup);
-  if (cnt <= 0) return;
-  const int s = it.slot;
-  const int r = slot_rank(p.ranks, s, p.r_max);
-  if (r == 0) return;
-  const int slice = blockIdx.y;
-  const int d0 = blockIdx.z * d_chunk;
-  const int dlen = min(d_chunk, p.D - d0);
-  if (dlen <= 0) return;
-
+  const int sub_per_item = use_tiles ? kTile / kGroup : 1;
+  const int64_t n_units = (int64_t)record_items(p.rec, p.T, p.S, use_tiles != 0) * sub_per_item;
+  const WorkRange R = xcd_work_range(n_units * nsplit * p.n_slices);
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   const int wave = tid >> 6;
+
+  for (int64_t w = R.begin; w < R.end; w += R.step) {
+  const int64_t unit = w % n_units;
+  const int64_t rest = w / n_units;
+  const int split = (int)(rest % nsplit);
+  const int slice = (int)(rest / nsplit);
+  const int64_t item_id = unit / sub_per_item;
+  const int sub = (int)(unit - item_id * sub_per_item);
+  Item it;
+  if (!read_item(p.rec, p.T, p.S, use_tiles != 0, item_id, it)) continue;
+  const int cnt = min(kGroup, it.cnt - sub * kGroup);
+  if (cnt <= 0) continue;
+  const int s = it.slot;
+  const int r = slot_rank(p.ranks, s, p.r_max);
+  if (r == 0) continue;
+  const int d0 = split * d_chunk;
+  const int dlen = min(d_chunk, p.D - d0);
+  if (dlen <= 0) continue;
+
   if (tid < kGroup) s_tok[tid] = tid < cnt ? load_token(p.rec, p.T, L.perm, it.p0 + sub * kGroup + tid) : 0;
   __syncthreads();
 
-  // stage the group's x rows for [d0, d0 + dlen)
+  // stage the group's x rows for [d0, d0 + dlen): every load is issued before
+  // the first LDS store, so the staging costs one memory round trip
   {
+    constexpr int kPerThread = kGroup * kXChunkBytes / 16 / kThreads;  // 8
     const int vecs_per_row = dlen / kVec;
+    const int total = cnt * vecs_per_row;
     const Elem* xb = reinterpret_cast<const Elem*>(p.x);
-    for (int e = tid; e < cnt * vecs_per_row; e += kThreads) {
-      const int g = e / vecs_per_row;
-      const int c = e - g * vecs_per_row;
-      const Elem* src = xb + (int64_t)s_tok[g] * p.ldx + d0 + c * kVec;
-      *reinterpret_cast<u32x4*>(&s_x[g][c * kVec]) = ld16(src);
+    u32x4 tmp[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int e = tid + j * kThreads;
+      if (e < total) {
+        const int g = e / vecs_per_row;
+        const int c = e - g * vecs_per_row;
+        tmp[j] = ld16(xb + (int64_t)s_tok[g] * p.ldx + d0 + c * kVec);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int e = tid + j * kThreads;
+      if (e < total) {
+        const int g = e / vecs_per_row;
+        const int c = e - g * vecs_per_row;
+        *reinterpret_cast<u32x4*>(&s_x[g][c * kVec]) = tmp[j];
+      }
     }
   }
   __syncthreads();
@@ -116,17 +146,27 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(ShrinkParams p, i
 #pragma unroll
     for (int q = 0; q < kRowsPerPass; ++q) krow[q] = (pass * kRowsPerPass + q) * kWavesPerWG + wave;
 
-    for (int dd = lane * kVec; dd < dlen; dd += 64 * kVec) {
-      u32x4 a[kRowsPerPass];
+    constexpr int kSteps = kChunkElems / (64 * kVec);  // 16-byte steps per lane per chunk
+    u32x4 a[kSteps][kRowsPerPass];
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int dd = (st * 64 + lane) * kVec;
 #pragma unroll
       for (int q = 0; q < kRowsPerPass; ++q)
-        a[q] = krow[q] < r ? ld16(Ab + (int64_t)krow[q] * p.D + d0 + dd) : u32x4{0, 0, 0, 0};
+        a[st][q] = (krow[q] < r && dd < dlen) ? ld16(Ab + (int64_t)krow[q] * p.D + d0 + dd) : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
-      for (int g = 0; g < kGroup; ++g) {
-        if (g < cnt) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(&s_x[g][dd]);
+    for (int st = 0; st < kSteps; ++st) {
+      const int dd = (st * 64 + lane) * kVec;
+      if (dd < dlen) {
 #pragma unroll
-          for (int q = 0; q < kRowsPerPass; ++q) acc[q * kGroup + g] = Tr::dot(a[q], xv, acc[q * kGroup + g]);
+        for (int g = 0; g < kGroup; ++g) {
+          if (g < cnt) {
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(&s_x[g][dd]);
+#pragma unroll
+            for (int q = 0; q < kRowsPerPass; ++q)
+              acc[q * kGroup + g] = Tr::dot(a[st][q], xv, acc[q * kGroup + g]);
+          }
         }
       }
     }
@@ -139,78 +179,106 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(ShrinkParams p, i
       else *dst = sum * sc;
     }
   }
-}
-
-template <typename Elem>
-__device__ inline void store_y4(Elem* dst, const float* acc, const Elem* src);
-
-template <>
-__device__ inline void store_y4<float>(float* dst, const float* acc, const float* src) {
-  f32x4 y = *reinterpret_cast<const f32x4*>(src);
-  y[0] += acc[0];
-  y[1] += acc[1];
-  y[2] += acc[2];
-  y[3] += acc[3];
-  *reinterpret_cast<f32x4*>(dst) = y;
-}
-
-template <typename Elem>
-__device__ inline void store_y4(Elem* dst, const float* acc, const Elem* src) {
-  using Tr = Traits<Elem>;
-  const u32x2 yv = *reinterpret_cast<const u32x2*>(src);
-  float y0 = Tr::elem_to_float(yv[0] & 0xffffu) + acc[0];
-  float y1 = Tr::elem_to_float(yv[0] >> 16) + acc[1];
-  float y2 = Tr::elem_to_float(yv[1] & 0xffffu) + acc[2];
-  float y3 = Tr::elem_to_float(yv[1] >> 16) + acc[3];
-  u32x2 o;
-  if constexpr (Tr::kDtype == LORA_BF16) {
-    o[0] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
-    o[1] = float_to_bf16_bits(y2) | (float_to_bf16_bits(y3) << 16);
-  } else {
-    o[0] = float_to_f16_bits(y0) | (float_to_f16_bits(y1) << 16);
-    o[1] = float_to_f16_bits(y2) | (float_to_f16_bits(y3) << 16);
+  __syncthreads();  // the next work item reuses s_tok and s_x
   }
-  *reinterpret_cast<u32x2*>(dst) = o;
 }
 
-constexpr int kColsPerLane = 4;
-constexpr int kExpandCols = kThreads * kColsPerLane;  // 1024 output columns per workgroup
-constexpr int kKChunk = 8;                            // rank elements per B load step
+// 4 consecutive y elements: 16 bytes of fp32 or 8 bytes of a 16-bit type.
+template <typename Elem> struct YChunk { typedef u32x2 type; };
+template <> struct YChunk<float> { typedef f32x4 type; };
+
+// y += acc for 4 consecutive elements, one rounding per element.
+template <typename Elem>
+__device__ inline void store_y4(Elem* dst, const float* acc, typename YChunk<Elem>::type yv) {
+  if constexpr (sizeof(Elem) == 4) {
+    f32x4 y = yv;
+    y[0] += acc[0];
+    y[1] += acc[1];
+    y[2] += acc[2];
+    y[3] += acc[3];
+    *reinterpret_cast<f32x4*>(dst) = y;
+  } else {
+    using Tr = Traits<Elem>;
+    const uint32_t w0 = yv[0], w1 = yv[1];
+    const float y0 = Tr::elem_to_float(w0 & 0xffffu) + acc[0];
+    const float y1 = Tr::elem_to_float(w0 >> 16) + acc[1];
+    const float y2 = Tr::elem_to_float(w1 & 0xffffu) + acc[2];
+    const float y3 = Tr::elem_to_float(w1 >> 16) + acc[3];
+    u32x2 o;
+    if constexpr (Tr::kDtype == LORA_BF16) {
+      o[0] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
+      o[1] = float_to_bf16_bits(y2) | (float_to_bf16_bits(y3) << 16);
+    } else {
+      o[0] = float_to_f16_bits(y0) | (float_to_f16_bits(y1) << 16);
+      o[1] = float_to_f16_bits(y2) | (float_to_f16_bits(y3) << 16);
+    }
+    *reinterpret_cast<u32x2*>(dst) = o;
+  }
+}
+
 
 template <typename Elem>
-__global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(ExpandParams p, int which_list, int sub_per_item) {
+__global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(ExpandParams p, int use_tiles, int n_ct) {
   using Tr = Traits<Elem>;
   __shared__ __attribute__((aligned(16))) float s_v[kGroup][LORA_MAX_RANK];
   __shared__ int s_tok[kGroup];
 
+  // work list: (16-token unit, column tile, slice), unit fastest
   const SegLayout L = seg_layout(p.T, p.S);
-  const int item_id = blockIdx.x / sub_per_item;
+  const int sub_per_item = use_tiles ? kTile / kGroup : 1;
+  const int64_t n_units = (int64_t)record_items(p.rec, p.T, p.S, use_tiles != 0) * sub_per_item;
+  const WorkRange R = xcd_work_range(n_units * n_ct * p.n_slices);
+  const int tid = threadIdx.x;
+
+  for (int64_t w = R.begin; w < R.end; w += R.step) {
+  const int64_t unit = w % n_units;
+  const int64_t rest = w / n_units;
+  const int ct = (int)(rest % n_ct);
+  const int slice = (int)(rest / n_ct);
+  const int64_t item_id = unit / sub_per_item;
+  const int sub = (int)(unit - item_id * sub_per_item);
   Item it;
-  if (!load_item(p.rec, p.T, p.S, which_list != 0, item_id, it)) return;
-  const int sub = blockIdx.x - item_id * sub_per_item;
+  if (!read_item(p.rec, p.T, p.S, use_tiles != 0, item_id, it)) continue;
   const int cnt = min(kGroup, it.cnt - sub * kGroup);
-  if (cnt <= 0) return;
-  const int slice = blockIdx.y;
+  if (cnt <= 0) continue;
   const int out = (int)p.out_size[slice];
-  const int j0 = blockIdx.z * kExpandCols;
-  if (j0 >= out) return;
+  const int j0 = ct * kExpandCols;
+  if (j0 >= out) continue;
   const int s = it.slot;
   const int r = slot_rank(p.ranks, s, p.r_max);
-  if (r == 0) return;
+  if (r == 0) continue;
 
-  const int tid = threadIdx.x;
   if (tid < kGroup) s_tok[tid] = tid < cnt ? load_token(p.rec, p.T, L.perm, it.p0 + sub * kGroup + tid) : 0;
   __syncthreads();
   const float* vb = p.v + (int64_t)slice * p.v_slice_stride;
-  for (int e = tid; e < kGroup * LORA_MAX_RANK; e += kThreads) {
-    const int g = e / LORA_MAX_RANK, k = e % LORA_MAX_RANK;
-    s_v[g][k] = (g < cnt && k < r) ? vb[(int64_t)s_tok[g] * p.r_max + k] : 0.f;
+  {
+    constexpr int kPerThread = kGroup * LORA_MAX_RANK / kThreads;  // 4
+    float tmp[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int e = tid + j * kThreads;
+      const int g = e / LORA_MAX_RANK, k = e % LORA_MAX_RANK;
+      tmp[j] = (g < cnt && k < r) ? vb[(int64_t)s_tok[g] * p.r_max + k] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int e = tid + j * kThreads;
+      s_v[e / LORA_MAX_RANK][e % LORA_MAX_RANK] = tmp[j];
+    }
   }
   __syncthreads();
 
   const int j = j0 + tid * kColsPerLane;
-  if (j >= out) return;
+  if (j < out) {
   const Elem* Bb = reinterpret_cast<const Elem*>(p.B[slice]) + ((int64_t)s * out + j) * p.r_max;
+  Elem* yb = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + j;
+  // the group's y values are loaded before any store, so the loads of all
+  // tokens are in flight together
+  typedef typename YChunk<Elem>::type ychunk_t;
+  ychunk_t ysave[kGroup];
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g)
+    if (g < cnt) ysave[g] = *reinterpret_cast<const ychunk_t*>(yb + (int64_t)s_tok[g] * p.ldy);
   float acc[kGroup][kColsPerLane];
 #pragma unroll
   for (int g = 0; g < kGroup; ++g)
@@ -257,13 +325,11 @@ __global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(ExpandParams p, i
     }
   }
 
-  Elem* yb = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + j;
 #pragma unroll
-  for (int g = 0; g < kGroup; ++g) {
-    if (g < cnt) {
-      Elem* row = yb + (int64_t)s_tok[g] * p.ldy;
-      store_y4<Elem>(row, acc[g], row);
-    }
+  for (int g = 0; g < kGroup; ++g)
+    if (g < cnt) store_y4<Elem>(yb + (int64_t)s_tok[g] * p.ldy, acc[g], ysave[g]);
+  }
+  __syncthreads();  // the next work item reuses s_tok and s_v
   }
 }
 
@@ -282,9 +348,10 @@ hipError_t shrink_launch(const ShrinkParams& p, bool tiles, hipStream_t stream) 
   const int64_t cap = tiles ? L.cap_tiles : L.cap_groups;
   const int chunk = kXChunkBytes / (int)sizeof(Elem);
   const int nsplit = (int)ceil_div(p.D, chunk);
-  dim3 grid((unsigned)(cap * sub), (unsigned)p.n_slices, (unsigned)nsplit);
-  hipLaunchKernelGGL(bgmv_shrink_kernel<Elem>, grid, dim3(kThreads), 0, stream, p, tiles ? 1 : 0, sub, chunk,
-                     nsplit > 1 ? 1 : 0);
+  const int grid = persistent_grid(reinterpret_cast<const void*>(&bgmv_shrink_kernel<Elem>), kThreads, 0,
+                                   cap * sub * nsplit * p.n_slices);
+  hipLaunchKernelGGL(bgmv_shrink_kernel<Elem>, dim3(grid), dim3(kThreads), 0, stream, p, tiles ? 1 : 0, nsplit,
+                     chunk, nsplit > 1 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -295,8 +362,10 @@ hipError_t expand_launch(const ExpandParams& p, bool tiles, hipStream_t stream) 
   const int64_t cap = tiles ? L.cap_tiles : L.cap_groups;
   int64_t max_out = 0;
   for (int i = 0; i < p.n_slices; ++i) max_out = p.out_size[i] > max_out ? p.out_size[i] : max_out;
-  dim3 grid((unsigned)(cap * sub), (unsigned)p.n_slices, (unsigned)ceil_div(max_out, kExpandCols));
-  hipLaunchKernelGGL(bgmv_expand_kernel<Elem>, grid, dim3(kThreads), 0, stream, p, tiles ? 1 : 0, sub);
+  const int n_ct = (int)ceil_div(max_out, kExpandCols);
+  const int grid = persistent_grid(reinterpret_cast<const void*>(&bgmv_expand_kernel<Elem>), kThreads, 0,
+                                   cap * sub * n_ct * p.n_slices);
+  hipLaunchKernelGGL(bgmv_expand_kernel<Elem>, dim3(grid), dim3(kThreads), 0, stream, p, tiles ? 1 : 0, n_ct);
   return hipGetLastError();
 }
 

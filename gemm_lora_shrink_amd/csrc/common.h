@@ -186,26 +186,49 @@ struct ExpandParams {
   int32_t S, r_max, n_slices, T;
 };
 
-// Reads work item `item_id` of a record and checks it against the call's sizes.
-// Returns false (the workgroup then does nothing) when the item does not exist,
-// when the record was built for other sizes, or when its fields are out of
-// range, so a wrong record can never make a kernel touch memory outside the
-// caller's buffers.
-__device__ inline bool load_item(const int32_t* rec, int T, int S, bool tiles, int64_t item_id, Item& it) {
-  if (rec[kBuiltT] != T || rec[kBuiltS] != S) return false;
-  const int n_items = rec[tiles ? kNumTiles : kNumGroups];
-  if (item_id >= n_items) return false;
-  const SegLayout L = seg_layout(T, S);
-  if (n_items > (tiles ? L.cap_tiles : L.cap_groups)) return false;
-  it = reinterpret_cast<const Item*>(rec + (tiles ? L.tiles : L.groups))[item_id];
-  const int cap = tiles ? kTile : kGroup;
-  return it.slot >= 0 && it.slot < S && it.p0 >= 0 && it.cnt > 0 && it.cnt <= cap && it.p0 + it.cnt <= T;
-}
-
 // Token index stored at perm position `pos`, clamped into [0, T).
 __device__ inline int load_token(const int32_t* rec, int T, int64_t perm_off, int pos) {
   const int t = rec[perm_off + pos];
   return t < 0 ? 0 : (t >= T ? T - 1 : t);
+}
+
+// Persistent work loops.  A launch has a fixed number of workgroups (a
+// multiple of 8, sized to what the chip holds at once) and walks a work list
+// whose length is only known on the device.  The hardware hands workgroup b
+// to XCD b % 8, and each of the 8 XCDs has its own L2, so XCD x is given the
+// contiguous range [x N / 8, (x + 1) N / 8) of the list and its workgroups
+// stride through it: consecutive work items (which share adapter rows or
+// activation rows) then meet in the same L2.  Every workgroup leaves the loop
+// after at most ceil(N / gridDim.x) + 1 items.
+constexpr int kXcds = 8;
+
+struct WorkRange {
+  int64_t begin, end, step;
+};
+
+__device__ inline WorkRange xcd_work_range(int64_t n_work) {
+  const int64_t xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds, wgs = gridDim.x / kXcds;
+  const int64_t per = n_work / kXcds, rem = n_work % kXcds;
+  const int64_t start = xcd * per + (xcd < rem ? xcd : rem);
+  const int64_t len = per + (xcd < rem ? 1 : 0);
+  return WorkRange{start + lb, start + len, wgs};
+}
+
+// Number of items in a record's list, or 0 when the record does not match
+// the call's sizes or its count is out of range.
+__device__ inline int record_items(const int32_t* rec, int T, int S, bool tiles) {
+  if (rec[kBuiltT] != T || rec[kBuiltS] != S) return 0;
+  const int n = rec[tiles ? kNumTiles : kNumGroups];
+  const SegLayout L = seg_layout(T, S);
+  return (n < 0 || n > (tiles ? L.cap_tiles : L.cap_groups)) ? 0 : n;
+}
+
+// Item `i` (< record_items) of a list, with its fields checked against the sizes.
+__device__ inline bool read_item(const int32_t* rec, int T, int S, bool tiles, int64_t i, Item& it) {
+  const SegLayout L = seg_layout(T, S);
+  it = reinterpret_cast<const Item*>(rec + (tiles ? L.tiles : L.groups))[i];
+  const int cap = tiles ? kTile : kGroup;
+  return it.slot >= 0 && it.slot < S && it.p0 >= 0 && it.cnt > 0 && it.cnt <= cap && it.p0 + it.cnt <= T;
 }
 
 __device__ inline int slot_rank(const int32_t* ranks, int s, int r_max) {
@@ -214,6 +237,11 @@ __device__ inline int slot_rank(const int32_t* ranks, int s, int r_max) {
   return r < 0 ? 0 : (r > r_max ? r_max : r);
 }
 
+// Workgroups of a persistent launch of `kernel`: as many as the chip holds at
+// once (occupancy x compute units of the current device), a multiple of 8,
+// and no more than `max_useful` rounded up to a multiple of 8.
+int persistent_grid(const void* kernel, int block, size_t dyn_lds, int64_t max_useful);
+
 // Host-side launchers (defined in the .hip files).
 hipError_t launch_build_segments(const int32_t* idx, int32_t T, int32_t S, int32_t mode, int32_t* rec,
                                  hipStream_t stream);
@@ -221,6 +249,8 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_bgmv_shrink(lora_dtype dt, const ShrinkParams& p, bool tiles, hipStream_t stream);
 hipError_t launch_bgmv_expand(lora_dtype dt, const ExpandParams& p, bool tiles, hipStream_t stream);
 hipError_t launch_sgmv_shrink(lora_dtype dt, const ShrinkParams& p, hipStream_t stream);
-hipError_t launch_sgmv_expand(lora_dtype dt, const ExpandParams& p, hipStream_t stream);
+// Matrix-core expand over the gather groups and/or the segmented tiles, in one
+// launch (16-bit types only).
+hipError_t launch_mfma_expand(lora_dtype dt, const ExpandParams& p, bool groups, bool tiles, hipStream_t stream);
 
 }  // namespace lora

@@ -1,14 +1,431 @@
-// Segmented path (SGMV) for long slot segments.
+// Segmented path (SGMV) on the matrix cores: per slot segment the shrink and
+// the expand are dense contractions, so they run on v_mfma_f32_16x16x32
+// (bf16 or fp16 inputs, fp32 accumulation).  The gather kernel is not efficient
+// for prefill, and the earlier segmented kernel lost accuracy by keeping the
+// intermediate in half precision ("Add multi-LoRA support", Limitations); here
+// the intermediate stays fp32 end to end.
+//
+// MFMA 16x16x32 lane layout (checked on gfx950): for D = A(16x32) * B(32x16),
+// lane l holds A[l%16][8*(l/16) + i], B[8*(l/16) + i][l%16] (i < 8) and
+// D[4*(l/16) + i][l%16] (i < 4).
+//
+// Shrink (tiles of up to 64 tokens of one slot, one slice per workgroup):
+//   D[token][rank] = sum_d x[token][d] * A[s][rank][d].  Wave w owns tokens
+//   16w..16w+15 and all ranks.  x rows are gathered straight from global memory
+//   into the A-operand registers (each lane loads 128 contiguous bytes of its
+//   row per 256-element chunk; the contraction index is permuted identically on
+//   both operands).  The slot's A chunk (64 ranks x 256) is shared by the four
+//   waves through LDS, double-buffered, with rows padded by 16 bytes so the
+//   operand reads are conflict-free.  One barrier per chunk; the next chunk's
+//   global loads are in flight while the current one is multiplied.
+//
+// Expand (work items of up to 16 or 64 tokens):
+//   y^T[j][token] += sum_k B[s][j][k] * v[token][k] -- the transposed product,
+//   so that each lane's four accumulators are four consecutive y columns of one
+//   token.  The fp32 intermediate enters the matrix core as v = hi + lo, both
+//   16-bit (two MFMAs), which keeps about 16 significant bits of v instead of
+//   re-rounding it to 8 or 11.  For fp16 each token row is first scaled by a
+//   power of two so that its largest value lies in [1, 2): hi and lo then stay
+//   in fp16's normal range whatever the magnitude of v, and the scale is undone
+//   exactly on the fp32 result.
 #include "common.h"
 
 namespace lora {
 
-hipError_t launch_sgmv_shrink(lora_dtype dt, const ShrinkParams& p, hipStream_t stream) {
-  return launch_bgmv_shrink(dt, p, /*tiles=*/true, stream);
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename Elem> struct Mfma;
+template <> struct Mfma<bf16_t> {
+  typedef bf16x8 vec;
+  __device__ static inline f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<half_t> {
+  typedef f16x8 vec;
+  __device__ static inline f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+template <typename V> __device__ inline V as_vec(u32x4 u) { return __builtin_bit_cast(V, u); }
+
+// Zero the 16-bit elements k0 + e (e < 8) that are >= r.
+__device__ inline u32x4 mask_tail16(u32x4 u, int k0, int r) {
+  if (k0 + 8 <= r) return u;
+  if (k0 >= r) return u32x4{0, 0, 0, 0};
+  u32x4 o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t word = u[w];
+    const uint32_t lo = (k0 + 2 * w < r) ? (word & 0xffffu) : 0u;
+    const uint32_t hi = (k0 + 2 * w + 1 < r) ? (word & 0xffff0000u) : 0u;
+    o[w] = lo | hi;
+  }
+  return o;
 }
 
-hipError_t launch_sgmv_expand(lora_dtype dt, const ExpandParams& p, hipStream_t stream) {
-  return launch_bgmv_expand(dt, p, /*tiles=*/true, stream);
+// ---------------------------------------------------------------------------
+// Expand
+// ---------------------------------------------------------------------------
+// A workgroup owns (work item of up to 64 tokens, 256 output columns, slice);
+// wave w owns columns 64 w .. 64 w + 63 for every 16-token sub-block of the
+// item.  All of a wave's global loads (its B rows, the v rows and the y values
+// of every sub-block) are issued before the first MFMA.  y is read and written
+// in a lane-contiguous layout -- eight lanes cover one token's 64 columns (128
+// bytes) -- and the MFMA results reach that layout through a per-wave LDS
+// transpose, so every y access of a wave touches whole cache lines.
+constexpr int kExpandColsPerWave = 64;                         // 4 MFMA blocks of 16
+constexpr int kExpandColsPerWG = 4 * kExpandColsPerWave;       // 256
+constexpr int kSubs = kTile / 16;                              // 16-token sub-blocks per item
+constexpr int kTrRow = kExpandColsPerWave + 4;                 // padded fp32 LDS row
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles,
+                                                               int n_ct) {
+  using M = Mfma<Elem>;
+  using V = typename M::vec;
+  using Tr = Traits<Elem>;
+  __shared__ int s_tok[kTile];
+  __shared__ __attribute__((aligned(16))) float s_tr[4][16][kTrRow];
+
+  // work list: (item, column tile, slice), item fastest; the items are the
+  // gather groups followed by the segmented tiles.  Every XCD walks one
+  // contiguous range, so the items of one slot (adjacent in the lists) share
+  // their B rows in one L2.
+  const SegLayout L = seg_layout(p.T, p.S);
+  const int n_g = use_groups ? record_items(p.rec, p.T, p.S, false) : 0;
+  const int n_t = use_tiles ? record_items(p.rec, p.T, p.S, true) : 0;
+  const int64_t n_items = (int64_t)n_g + n_t;
+  const WorkRange R = xcd_work_range(n_items * n_ct * p.n_slices);
+  const int tid = threadIdx.x;
+
+  for (int64_t w = R.begin; w < R.end; w += R.step) {
+  const int64_t item = w % n_items;
+  const int64_t rest = w / n_items;
+  const int ct = (int)(rest % n_ct);
+  const int slice = (int)(rest / n_ct);
+  const bool tiles = item >= n_g;
+  Item it;
+  if (!read_item(p.rec, p.T, p.S, tiles, tiles ? item - n_g : item, it)) continue;
+  const int out = (int)p.out_size[slice];
+  const int c0 = ct * kExpandColsPerWG;
+  if (c0 >= out) continue;
+  const int s = it.slot;
+  const int r = slot_rank(p.ranks, s, p.r_max);
+  if (r == 0) continue;
+
+  if (tid < kTile) s_tok[tid] = tid < it.cnt ? load_token(p.rec, p.T, L.perm, it.p0 + tid) : -1;
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int jw = c0 + wave * kExpandColsPerWave;
+  const bool wave_on = jw < out;  // whole 64-column blocks: out is a multiple of 8, checked below per column
+  const int n = lane & 15, kg = lane >> 4;
+  const int nks = r > 32 ? 2 : 1;  // 32-wide rank steps
+  const int n_sub = (it.cnt + 15) >> 4;
+
+  // y, coalesced: lane covers token (lane / 8) + 8 h of the sub-block,
+  // columns 8 (lane % 8) .. +7 (16 bytes)
+  const int yr = lane >> 3, yc = (lane & 7) * 8;
+  Elem* yb = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + jw + yc;
+  const bool ycol_ok = wave_on && jw + yc < out;
+  u32x4 yold[kSubs][2];
+#pragma unroll
+  for (int sb = 0; sb < kSubs; ++sb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = sb < n_sub ? s_tok[sb * 16 + h * 8 + yr] : -1;
+      yold[sb][h] = (ycol_ok && t >= 0) ? ld16(yb + (int64_t)t * p.ldy) : u32x4{0, 0, 0, 0};
+    }
+
+  // A operand: this wave's 64 B rows (4 blocks x 16), both rank steps
+  const Elem* Bs = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max;
+  u32x4 braw[4][2];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int row = jw + cb * 16 + n;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int k0 = ks * 32 + kg * 8;
+      braw[cb][ks] = (wave_on && ks < nks && row < out && k0 < p.r_max) ? ld16(Bs + (int64_t)row * p.r_max + k0)
+                                                                         : u32x4{0, 0, 0, 0};
+    }
+  }
+  // B operand source: v[tok][32 ks + 8 kg .. +7] of every sub-block
+  const float* vb = p.v + (int64_t)slice * p.v_slice_stride;
+  f32x4 vraw[kSubs][2][2];
+#pragma unroll
+  for (int sb = 0; sb < kSubs; ++sb) {
+    const int tok = sb < n_sub ? s_tok[sb * 16 + n] : -1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int k0 = ks * 32 + kg * 8;
+      const bool ok = wave_on && tok >= 0 && ks < nks && k0 < p.r_max;
+      const float* src = vb + (int64_t)(tok >= 0 ? tok : 0) * p.r_max + k0;
+      vraw[sb][ks][0] = ok ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
+      vraw[sb][ks][1] = ok ? *reinterpret_cast<const f32x4*>(src + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  V bop[4][2];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) bop[cb][ks] = as_vec<V>(mask_tail16(braw[cb][ks], ks * 32 + kg * 8, r));
+
+#pragma unroll
+  for (int sb = 0; sb < kSubs; ++sb) {
+    if (sb >= n_sub) break;
+    float vv[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int k0 = ks * 32 + kg * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vv[ks][i] = (k0 + i < r) ? vraw[sb][ks][0][i] : 0.f;
+        vv[ks][4 + i] = (k0 + 4 + i < r) ? vraw[sb][ks][1][i] : 0.f;
+      }
+    }
+    // fp16: scale the token's row by a power of two so that |v| < 2
+    float unscale = 1.0f;
+    if constexpr (Tr::kDtype == LORA_F16) {
+      float mx = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(vv[ks][i]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (mx > 0.f) {
+        int e;
+        frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+        const float sc = ldexpf(1.0f, 1 - e);
+        unscale = ldexpf(1.0f, e - 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) vv[ks][i] *= sc;
+      }
+    }
+    V vhi[2], vlo[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const Elem h = static_cast<Elem>(vv[ks][i]);
+        vhi[ks][i] = h;
+        vlo[ks][i] = static_cast<Elem>(vv[ks][i] - static_cast<float>(h));
+      }
+    }
+    // D[column 4 kg + i][token n] of block cb -> s_tr[wave][n][16 cb + 4 kg + i]
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc = M::mma(bop[cb][0], vhi[0], acc);
+      acc = M::mma(bop[cb][0], vlo[0], acc);
+      if (nks > 1) {
+        acc = M::mma(bop[cb][1], vhi[1], acc);
+        acc = M::mma(bop[cb][1], vlo[1], acc);
+      }
+      acc *= unscale;
+      *reinterpret_cast<f32x4*>(&s_tr[wave][n][cb * 16 + kg * 4]) = acc;
+    }
+    __syncthreads();
+    // coalesced read-modify-write of y
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = s_tok[sb * 16 + h * 8 + yr];
+      if (ycol_ok && t >= 0) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&s_tr[wave][h * 8 + yr][yc]);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&s_tr[wave][h * 8 + yr][yc + 4]);
+        const float add[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t wd = yold[sb][h][q];
+          const float y0 = Tr::elem_to_float(wd & 0xffffu) + add[2 * q];
+          const float y1 = Tr::elem_to_float(wd >> 16) + add[2 * q + 1];
+          if constexpr (Tr::kDtype == LORA_BF16) o[q] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
+          else o[q] = float_to_f16_bits(y0) | (float_to_f16_bits(y1) << 16);
+        }
+        *reinterpret_cast<u32x4*>(yb + (int64_t)t * p.ldy) = o;
+      }
+    }
+    __syncthreads();
+  }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shrink
+// ---------------------------------------------------------------------------
+constexpr int kKC = 256;             // contraction elements per chunk
+constexpr int kLdsRow = kKC + 8;     // padded LDS row (elements)
+constexpr int kSteps = kKC / 32;     // MFMA steps per chunk
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void mfma_shrink_kernel(ShrinkParams p) {
+  using M = Mfma<Elem>;
+  using V = typename M::vec;
+  __shared__ __attribute__((aligned(16))) Elem s_a[2][kTile][kLdsRow];
+  __shared__ int s_tok[kTile];
+
+  // work list: (tile, slice), slice fastest, so the slices of one tile share
+  // its x rows and the tiles of one slot share its A rows in one L2
+  const SegLayout L = seg_layout(p.T, p.S);
+  const int64_t n_tiles = record_items(p.rec, p.T, p.S, true);
+  const WorkRange R = xcd_work_range(n_tiles * p.n_slices);
+  const int tid = threadIdx.x;
+
+  for (int64_t w = R.begin; w < R.end; w += R.step) {
+  const int64_t tile = w / p.n_slices;
+  const int slice = (int)(w - tile * p.n_slices);
+  Item it;
+  if (!read_item(p.rec, p.T, p.S, true, tile, it)) continue;
+  const int s = it.slot;
+  const int r = slot_rank(p.ranks, s, p.r_max);
+  if (r == 0) continue;
+
+  if (tid < kTile) s_tok[tid] = tid < it.cnt ? load_token(p.rec, p.T, L.perm, it.p0 + tid) : -1;
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, kg = lane >> 4;
+  const int tok = s_tok[wave * 16 + m];
+  const Elem* xrow = reinterpret_cast<const Elem*>(p.x) + (int64_t)(tok >= 0 ? tok : 0) * p.ldx;
+  const Elem* As = reinterpret_cast<const Elem*>(p.A[slice]) + (int64_t)s * p.r_max * p.D;
+  const int nb_used = (r + 15) >> 4;  // 16-rank blocks holding real ranks
+  const int a_rows = nb_used * 16;    // A rows staged (rows >= r read as zero)
+
+  // x: MFMA step j of a chunk takes elements 32 j + 8 kg .. +7 of the lane's
+  // row, so the four lanes of a row read 64 contiguous bytes per load.
+  // A: 16-byte piece q = j * 256 + tid of the chunk is row q / 32, piece q % 32,
+  // so each wave-wide load reads 1 KB of consecutive memory.
+  u32x4 xcur[kSteps], xnext[kSteps];
+  u32x4 ar[kSteps];
+  auto load_x = [&](int c, u32x4 (&xdst)[kSteps]) {
+    const int d0 = c * kKC;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int dx = d0 + 32 * j + 8 * kg;
+      xdst[j] = (tok >= 0 && dx < p.D) ? ld16(xrow + dx) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto load_a = [&](int c) {
+    const int d0 = c * kKC;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int q = j * kThreads + tid;
+      const int row = q >> 5, da = d0 + (q & 31) * 8;
+      ar[j] = (row < a_rows && row < r && da < p.D) ? ld16(As + (int64_t)row * p.D + da) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int q = j * kThreads + tid;
+      const int row = q >> 5;
+      if (row < a_rows) *reinterpret_cast<u32x4*>(&s_a[buf][row][(q & 31) * 8]) = ar[j];
+    }
+  };
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int n_chunks = (p.D + kKC - 1) / kKC;
+  load_x(0, xcur);
+  load_a(0);
+  store_a(0);
+  __syncthreads();
+  for (int c = 0; c < n_chunks; ++c) {
+    const int cur = c & 1;
+    const bool more = c + 1 < n_chunks;
+    if (more) {
+      load_x(c + 1, xnext);
+      load_a(c + 1);
+    }
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const V xo = as_vec<V>(xcur[j]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if (nb < nb_used) {
+          const V ao = as_vec<V>(*reinterpret_cast<const u32x4*>(&s_a[cur][nb * 16 + m][32 * j + 8 * kg]));
+          acc[nb] = M::mma(xo, ao, acc[nb]);
+        }
+      }
+    }
+    if (more) {
+      store_a(cur ^ 1);
+#pragma unroll
+      for (int j = 0; j < kSteps; ++j) xcur[j] = xnext[j];
+    }
+    __syncthreads();
+  }
+
+  // D[token row 4*kg + i][rank 16*nb + m] -> v
+  const float sc = p.scale ? p.scale[s] : 1.0f;
+  float* vout = p.v + (int64_t)slice * p.v_slice_stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = s_tok[wave * 16 + kg * 4 + i];
+    if (t < 0) continue;
+    float* vrow = vout + (int64_t)t * p.r_max;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int k = nb * 16 + m;
+      if (k < p.r_max) vrow[k] = k < r ? acc[nb][i] * sc : 0.f;
+    }
+  }
+  __syncthreads();  // the next work item reuses s_tok and s_a
+  }
+}
+
+template <typename Elem>
+hipError_t expand_launch(const ExpandParams& p, bool groups, bool tiles, hipStream_t stream) {
+  const SegLayout L = seg_layout(p.T, p.S);
+  int64_t max_out = 0;
+  for (int i = 0; i < p.n_slices; ++i) max_out = p.out_size[i] > max_out ? p.out_size[i] : max_out;
+  const int64_t cap = (groups ? L.cap_groups : 0) + (tiles ? L.cap_tiles : 0);
+  const int64_t n_ct = ceil_div(max_out, kExpandColsPerWG);
+  const int grid = persistent_grid(reinterpret_cast<const void*>(&mfma_expand_kernel<Elem>), kThreads, 0,
+                                   cap * n_ct * p.n_slices);
+  hipLaunchKernelGGL(mfma_expand_kernel<Elem>, dim3(grid), dim3(kThreads), 0, stream, p, groups ? 1 : 0,
+                     tiles ? 1 : 0, (int)n_ct);
+  return hipGetLastError();
+}
+
+template <typename Elem>
+hipError_t shrink_launch(const ShrinkParams& p, hipStream_t stream) {
+  const SegLayout L = seg_layout(p.T, p.S);
+  const int grid = persistent_grid(reinterpret_cast<const void*>(&mfma_shrink_kernel<Elem>), kThreads, 0,
+                                   L.cap_tiles * p.n_slices);
+  hipLaunchKernelGGL(mfma_shrink_kernel<Elem>, dim3(grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sgmv_shrink(lora_dtype dt, const ShrinkParams& p, hipStream_t stream) {
+  switch (dt) {
+    case LORA_F16: return shrink_launch<half_t>(p, stream);
+    case LORA_BF16: return shrink_launch<bf16_t>(p, stream);
+    default: return launch_bgmv_shrink(dt, p, /*tiles=*/true, stream);
+  }
+}
+
+hipError_t launch_mfma_expand(lora_dtype dt, const ExpandParams& p, bool groups, bool tiles, hipStream_t stream) {
+  switch (dt) {
+    case LORA_F16: return expand_launch<half_t>(p, groups, tiles, stream);
+    case LORA_BF16: return expand_launch<bf16_t>(p, groups, tiles, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace lora
