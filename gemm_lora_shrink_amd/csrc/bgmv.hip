@@ -152,8 +152,10 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(ShrinkParams p, i
     for (int st = 0; st < kSteps; ++st) {
       const int dd = (st * 64 + lane) * kVec;
 #pragma unroll
-      for (int q = 0; q < kRowsPerPass; ++q)
-        a[st][q] = (krow[q] < r && dd < dlen) ? ld16(Ab + (int64_t)krow[q] * p.D + d0 + dd) : u32x4{0, 0, 0, 0};
+      for (int q = 0; q < kRowsPerPass; ++q) {
+        const bool ok = krow[q] < r && dd < dlen;
+        a[st][q] = ld16_or0(Ab + (ok ? (int64_t)krow[q] * p.D + d0 + dd : 0), ok);
+      }
     }
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {

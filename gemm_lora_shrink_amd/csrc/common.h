@@ -86,6 +86,28 @@ __device__ inline uint32_t float_to_f16_bits(float f) {
 __device__ inline f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ inline bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 
+// Branch-free guarded loads.  A lane whose access is out of range reads 16
+// bytes of zeros from a small constant array instead, so the select is on the
+// address, before the load: no branch splits the code (the compiler would wait
+// for every outstanding load at the merge) and no select on the loaded value
+// forces a wait right after the load.
+__device__ const u32x4 g_zero16[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+
+// Both candidate addresses are global memory; saying so keeps the load a
+// global_load (a generic flat_load would also hold the LDS wait counter).
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+typedef __attribute__((address_space(1))) const f32x4 global_f32x4;
+
+__device__ inline u32x4 ld16_or0(const void* p, bool ok) {
+  const global_u32x4* gp = (const global_u32x4*)(ok ? p : static_cast<const void*>(g_zero16));
+  return *gp;
+}
+__device__ inline f32x4 ldf4_or0(const float* p, bool ok) {
+  const global_f32x4* gp =
+      (const global_f32x4*)(ok ? static_cast<const void*>(p) : static_cast<const void*>(g_zero16));
+  return *gp;
+}
+
 // Traits: Elem is the storage type; a "vec" is 16 bytes of it.
 template <typename Elem> struct Traits;
 

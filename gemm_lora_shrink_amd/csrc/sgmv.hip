@@ -72,192 +72,197 @@ __device__ inline u32x4 mask_tail16(u32x4 u, int k0, int r) {
 // ---------------------------------------------------------------------------
 // Expand
 // ---------------------------------------------------------------------------
-// A workgroup owns (work item of up to 64 tokens, 256 output columns, slice);
-// wave w owns columns 64 w .. 64 w + 63 for every 16-token sub-block of the
-// item.  All of a wave's global loads (its B rows, the v rows and the y values
-// of every sub-block) are issued before the first MFMA.  y is read and written
-// in a lane-contiguous layout -- eight lanes cover one token's 64 columns (128
-// bytes) -- and the MFMA results reach that layout through a per-wave LDS
-// transpose, so every y access of a wave touches whole cache lines.
+// Work unit: (item of up to 64 tokens, slice, a run of 256-column tiles).  Per
+// unit the workgroup reads the item's token list once and converts the item's
+// fp32 v rows once into the 16-bit hi/lo operands, kept in LDS for the four
+// waves.  Then, per column tile, wave w handles columns 64 w .. 64 w + 63:
+// it issues its y loads (lane-contiguous: eight lanes cover one token's 64
+// columns, 128 bytes) and its B-row loads first, runs the MFMAs per 16-token
+// sub-block, transposes the fp32 result through a wave-private LDS block and
+// updates y with 16-byte accesses.  No workgroup barrier is needed inside a
+// unit.
 constexpr int kExpandColsPerWave = 64;                         // 4 MFMA blocks of 16
 constexpr int kExpandColsPerWG = 4 * kExpandColsPerWave;       // 256
 constexpr int kSubs = kTile / 16;                              // 16-token sub-blocks per item
 constexpr int kTrRow = kExpandColsPerWave + 4;                 // padded fp32 LDS row
+constexpr int kVRow = LORA_MAX_RANK + 8;                       // padded 16-bit LDS row of v
 
 template <typename Elem>
-__global__ __launch_bounds__(kThreads) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles,
+__global__ __launch_bounds__(kThreads, 4) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles,
                                                                int n_ct) {
   using M = Mfma<Elem>;
   using V = typename M::vec;
   using Tr = Traits<Elem>;
   __shared__ int s_tok[kTile];
+  __shared__ float s_unscale[kTile];
+  __shared__ __attribute__((aligned(16))) Elem s_vhi[kTile][kVRow];
+  __shared__ __attribute__((aligned(16))) Elem s_vlo[kTile][kVRow];
   __shared__ __attribute__((aligned(16))) float s_tr[4][16][kTrRow];
 
-  // work list: (item, column tile, slice), item fastest; the items are the
-  // gather groups followed by the segmented tiles.  Every XCD walks one
-  // contiguous range, so the items of one slot (adjacent in the lists) share
-  // their B rows in one L2.
   const SegLayout L = seg_layout(p.T, p.S);
   const int n_g = use_groups ? record_items(p.rec, p.T, p.S, false) : 0;
   const int n_t = use_tiles ? record_items(p.rec, p.T, p.S, true) : 0;
   const int64_t n_items = (int64_t)n_g + n_t;
-  const WorkRange R = xcd_work_range(n_items * n_ct * p.n_slices);
+  // column tiles per unit: enough units to give every workgroup about two
+  const int64_t tile_slots = n_items * n_ct * p.n_slices;
+  int run = (int)(tile_slots / (2 * (int64_t)gridDim.x));
+  run = run < 1 ? 1 : (run > n_ct ? n_ct : run);
+  const int n_runs = (n_ct + run - 1) / run;
+  // unit order: item fastest, then column run, then slice
+  const WorkRange R = xcd_work_range(n_items * n_runs * p.n_slices);
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, kg = lane >> 4;
+  const int yr = lane >> 3, yc = (lane & 7) * 8;
+  const Elem* yzero = reinterpret_cast<const Elem*>(g_zero16);
 
   for (int64_t w = R.begin; w < R.end; w += R.step) {
   const int64_t item = w % n_items;
   const int64_t rest = w / n_items;
-  const int ct = (int)(rest % n_ct);
-  const int slice = (int)(rest / n_ct);
+  const int cr = (int)(rest % n_runs);
+  const int slice = (int)(rest / n_runs);
   const bool tiles = item >= n_g;
   Item it;
   if (!read_item(p.rec, p.T, p.S, tiles, tiles ? item - n_g : item, it)) continue;
   const int out = (int)p.out_size[slice];
-  const int c0 = ct * kExpandColsPerWG;
-  if (c0 >= out) continue;
+  const int ct_begin = cr * run;
+  const int ct_end = min(ct_begin + run, (int)ceil_div(out, kExpandColsPerWG));
+  if (ct_begin >= ct_end) continue;
   const int s = it.slot;
   const int r = slot_rank(p.ranks, s, p.r_max);
   if (r == 0) continue;
-
-  if (tid < kTile) s_tok[tid] = tid < it.cnt ? load_token(p.rec, p.T, L.perm, it.p0 + tid) : -1;
-  __syncthreads();
-
-  const int wave = tid >> 6, lane = tid & 63;
-  const int jw = c0 + wave * kExpandColsPerWave;
-  const bool wave_on = jw < out;  // whole 64-column blocks: out is a multiple of 8, checked below per column
-  const int n = lane & 15, kg = lane >> 4;
   const int nks = r > 32 ? 2 : 1;  // 32-wide rank steps
   const int n_sub = (it.cnt + 15) >> 4;
 
-  // y, coalesced: lane covers token (lane / 8) + 8 h of the sub-block,
-  // columns 8 (lane % 8) .. +7 (16 bytes)
-  const int yr = lane >> 3, yc = (lane & 7) * 8;
-  Elem* yb = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + jw + yc;
-  const bool ycol_ok = wave_on && jw + yc < out;
-  u32x4 yold[kSubs][2];
+  // token list and the item's v rows as hi + lo (thread: token tid / 4,
+  // ranks 16 (tid % 4) .. +15)
+  {
+    const int tt = tid >> 2, kq = (tid & 3) * 16;
+    const int tok = tt < it.cnt ? load_token(p.rec, p.T, L.perm, it.p0 + tt) : -1;
+    if ((tid & 3) == 0) s_tok[tt] = tok;
+    const float* src = p.v + (int64_t)slice * p.v_slice_stride + (int64_t)(tok >= 0 ? tok : 0) * p.r_max + kq;
+    float vv[16];
 #pragma unroll
-  for (int sb = 0; sb < kSubs; ++sb)
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = tok >= 0 && kq + 4 * q < p.r_max;
+      const f32x4 f = ldf4_or0(src + (ok ? 4 * q : 0), ok);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = sb < n_sub ? s_tok[sb * 16 + h * 8 + yr] : -1;
-      yold[sb][h] = (ycol_ok && t >= 0) ? ld16(yb + (int64_t)t * p.ldy) : u32x4{0, 0, 0, 0};
+      for (int e = 0; e < 4; ++e) vv[4 * q + e] = (kq + 4 * q + e < r) ? f[e] : 0.f;
     }
-
-  // A operand: this wave's 64 B rows (4 blocks x 16), both rank steps
-  const Elem* Bs = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max;
-  u32x4 braw[4][2];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int row = jw + cb * 16 + n;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int k0 = ks * 32 + kg * 8;
-      braw[cb][ks] = (wave_on && ks < nks && row < out && k0 < p.r_max) ? ld16(Bs + (int64_t)row * p.r_max + k0)
-                                                                         : u32x4{0, 0, 0, 0};
-    }
-  }
-  // B operand source: v[tok][32 ks + 8 kg .. +7] of every sub-block
-  const float* vb = p.v + (int64_t)slice * p.v_slice_stride;
-  f32x4 vraw[kSubs][2][2];
-#pragma unroll
-  for (int sb = 0; sb < kSubs; ++sb) {
-    const int tok = sb < n_sub ? s_tok[sb * 16 + n] : -1;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int k0 = ks * 32 + kg * 8;
-      const bool ok = wave_on && tok >= 0 && ks < nks && k0 < p.r_max;
-      const float* src = vb + (int64_t)(tok >= 0 ? tok : 0) * p.r_max + k0;
-      vraw[sb][ks][0] = ok ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
-      vraw[sb][ks][1] = ok ? *reinterpret_cast<const f32x4*>(src + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-
-  V bop[4][2];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) bop[cb][ks] = as_vec<V>(mask_tail16(braw[cb][ks], ks * 32 + kg * 8, r));
-
-#pragma unroll
-  for (int sb = 0; sb < kSubs; ++sb) {
-    if (sb >= n_sub) break;
-    float vv[2][8];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int k0 = ks * 32 + kg * 8;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vv[ks][i] = (k0 + i < r) ? vraw[sb][ks][0][i] : 0.f;
-        vv[ks][4 + i] = (k0 + 4 + i < r) ? vraw[sb][ks][1][i] : 0.f;
-      }
-    }
-    // fp16: scale the token's row by a power of two so that |v| < 2
     float unscale = 1.0f;
     if constexpr (Tr::kDtype == LORA_F16) {
+      // scale the token's row by a power of two so that |v| < 2
       float mx = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(vv[ks][i]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(vv[e]));
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
       if (mx > 0.f) {
-        int e;
-        frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
-        const float sc = ldexpf(1.0f, 1 - e);
-        unscale = ldexpf(1.0f, e - 1);
+        int ex;
+        frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
+        const float sc = ldexpf(1.0f, 1 - ex);
+        unscale = ldexpf(1.0f, ex - 1);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) vv[ks][i] *= sc;
+        for (int e = 0; e < 16; ++e) vv[e] *= sc;
       }
     }
-    V vhi[2], vlo[2];
+    if ((tid & 3) == 0) s_unscale[tt] = unscale;
+    V hi0, hi1, lo0, lo1;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const Elem h = static_cast<Elem>(vv[ks][i]);
-        vhi[ks][i] = h;
-        vlo[ks][i] = static_cast<Elem>(vv[ks][i] - static_cast<float>(h));
-      }
+    for (int e = 0; e < 8; ++e) {
+      const Elem h0 = static_cast<Elem>(vv[e]), h1 = static_cast<Elem>(vv[8 + e]);
+      hi0[e] = h0;
+      hi1[e] = h1;
+      lo0[e] = static_cast<Elem>(vv[e] - static_cast<float>(h0));
+      lo1[e] = static_cast<Elem>(vv[8 + e] - static_cast<float>(h1));
     }
-    // D[column 4 kg + i][token n] of block cb -> s_tr[wave][n][16 cb + 4 kg + i]
+    *reinterpret_cast<V*>(&s_vhi[tt][kq]) = hi0;
+    *reinterpret_cast<V*>(&s_vhi[tt][kq + 8]) = hi1;
+    *reinterpret_cast<V*>(&s_vlo[tt][kq]) = lo0;
+    *reinterpret_cast<V*>(&s_vlo[tt][kq + 8]) = lo1;
+  }
+  __syncthreads();
+
+  const Elem* Bs = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max;
+  Elem* ybase = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + yc;
+  for (int ct = ct_begin; ct < ct_end; ++ct) {
+    const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
+    const bool ycol_ok = jw + yc < out;  // out is a multiple of 8
+    // y of every sub-block, first
+    u32x4 yold[kSubs][2];
+#pragma unroll
+    for (int sb = 0; sb < kSubs; ++sb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = sb < n_sub ? s_tok[sb * 16 + h * 8 + yr] : -1;
+        const bool ok = ycol_ok && t >= 0;
+        yold[sb][h] = ld16_or0(ok ? ybase + jw + (int64_t)t * p.ldy : yzero, ok);
+      }
+    // A operand: this wave's 64 B rows (4 blocks x 16), both rank steps
+    V bop[4][2];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc = M::mma(bop[cb][0], vhi[0], acc);
-      acc = M::mma(bop[cb][0], vlo[0], acc);
-      if (nks > 1) {
-        acc = M::mma(bop[cb][1], vhi[1], acc);
-        acc = M::mma(bop[cb][1], vlo[1], acc);
-      }
-      acc *= unscale;
-      *reinterpret_cast<f32x4*>(&s_tr[wave][n][cb * 16 + kg * 4]) = acc;
-    }
-    __syncthreads();
-    // coalesced read-modify-write of y
+      const int row = jw + cb * 16 + n;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = s_tok[sb * 16 + h * 8 + yr];
-      if (ycol_ok && t >= 0) {
+      for (int ks = 0; ks < 2; ++ks) {
+        const int k0 = ks * 32 + kg * 8;
+        const bool ok = ks < nks && row < out && k0 < p.r_max;
+        bop[cb][ks] = as_vec<V>(mask_tail16(ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok), k0, r));
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < kSubs; ++sb) {
+      if (sb >= n_sub) break;
+      // B operand: v[tok 16 sb + n][32 ks + 8 kg .. +7], hi and lo
+      V vhi[2], vlo[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        vhi[ks] = *reinterpret_cast<const V*>(&s_vhi[sb * 16 + n][ks * 32 + kg * 8]);
+        vlo[ks] = *reinterpret_cast<const V*>(&s_vlo[sb * 16 + n][ks * 32 + kg * 8]);
+      }
+      const float unscale = s_unscale[sb * 16 + n];
+      // D[column 4 kg + i][token n] of block cb -> s_tr[wave][n][16 cb + 4 kg + i]
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc = M::mma(bop[cb][0], vhi[0], acc);
+        acc = M::mma(bop[cb][0], vlo[0], acc);
+        if (nks > 1) {
+          acc = M::mma(bop[cb][1], vhi[1], acc);
+          acc = M::mma(bop[cb][1], vlo[1], acc);
+        }
+        acc *= unscale;
+        *reinterpret_cast<f32x4*>(&s_tr[wave][n][cb * 16 + kg * 4]) = acc;
+      }
+      // the block is written and read by this wave only
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = s_tok[sb * 16 + h * 8 + yr];
         const f32x4 a0 = *reinterpret_cast<const f32x4*>(&s_tr[wave][h * 8 + yr][yc]);
         const f32x4 a1 = *reinterpret_cast<const f32x4*>(&s_tr[wave][h * 8 + yr][yc + 4]);
-        const float add[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        u32x4 o;
+        if (ycol_ok && t >= 0) {
+          const float add[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t wd = yold[sb][h][q];
-          const float y0 = Tr::elem_to_float(wd & 0xffffu) + add[2 * q];
-          const float y1 = Tr::elem_to_float(wd >> 16) + add[2 * q + 1];
-          if constexpr (Tr::kDtype == LORA_BF16) o[q] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
-          else o[q] = float_to_f16_bits(y0) | (float_to_f16_bits(y1) << 16);
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t wd = yold[sb][h][q];
+            const float y0 = Tr::elem_to_float(wd & 0xffffu) + add[2 * q];
+            const float y1 = Tr::elem_to_float(wd >> 16) + add[2 * q + 1];
+            if constexpr (Tr::kDtype == LORA_BF16) o[q] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
+            else o[q] = float_to_f16_bits(y0) | (float_to_f16_bits(y1) << 16);
+          }
+          *reinterpret_cast<u32x4*>(ybase + jw + (int64_t)t * p.ldy) = o;
         }
-        *reinterpret_cast<u32x4*>(yb + (int64_t)t * p.ldy) = o;
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __syncthreads();
   }
+  __syncthreads();  // the next unit rewrites s_tok and the v operands
   }
 }
 
@@ -299,8 +304,6 @@ __global__ __launch_bounds__(kThreads) void mfma_shrink_kernel(ShrinkParams p) {
   const int tok = s_tok[wave * 16 + m];
   const Elem* xrow = reinterpret_cast<const Elem*>(p.x) + (int64_t)(tok >= 0 ? tok : 0) * p.ldx;
   const Elem* As = reinterpret_cast<const Elem*>(p.A[slice]) + (int64_t)s * p.r_max * p.D;
-  const int nb_used = (r + 15) >> 4;  // 16-rank blocks holding real ranks
-  const int a_rows = nb_used * 16;    // A rows staged (rows >= r read as zero)
 
   // x: MFMA step j of a chunk takes elements 32 j + 8 kg .. +7 of the lane's
   // row, so the four lanes of a row read 64 contiguous bytes per load.
@@ -313,7 +316,8 @@ __global__ __launch_bounds__(kThreads) void mfma_shrink_kernel(ShrinkParams p) {
 #pragma unroll
     for (int j = 0; j < kSteps; ++j) {
       const int dx = d0 + 32 * j + 8 * kg;
-      xdst[j] = (tok >= 0 && dx < p.D) ? ld16(xrow + dx) : u32x4{0, 0, 0, 0};
+      const bool ok = tok >= 0 && dx < p.D;
+      xdst[j] = ld16_or0(xrow + (ok ? dx : 0), ok);
     }
   };
   auto load_a = [&](int c) {
@@ -322,15 +326,15 @@ __global__ __launch_bounds__(kThreads) void mfma_shrink_kernel(ShrinkParams p) {
     for (int j = 0; j < kSteps; ++j) {
       const int q = j * kThreads + tid;
       const int row = q >> 5, da = d0 + (q & 31) * 8;
-      ar[j] = (row < a_rows && row < r && da < p.D) ? ld16(As + (int64_t)row * p.D + da) : u32x4{0, 0, 0, 0};
+      const bool ok = row < r && da < p.D;
+      ar[j] = ld16_or0(As + (ok ? (int64_t)row * p.D + da : 0), ok);
     }
   };
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < kSteps; ++j) {
       const int q = j * kThreads + tid;
-      const int row = q >> 5;
-      if (row < a_rows) *reinterpret_cast<u32x4*>(&s_a[buf][row][(q & 31) * 8]) = ar[j];
+      *reinterpret_cast<u32x4*>(&s_a[buf][q >> 5][(q & 31) * 8]) = ar[j];
     }
   };
 
@@ -355,10 +359,8 @@ __global__ __launch_bounds__(kThreads) void mfma_shrink_kernel(ShrinkParams p) {
       const V xo = as_vec<V>(xcur[j]);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        if (nb < nb_used) {
-          const V ao = as_vec<V>(*reinterpret_cast<const u32x4*>(&s_a[cur][nb * 16 + m][32 * j + 8 * kg]));
-          acc[nb] = M::mma(xo, ao, acc[nb]);
-        }
+        const V ao = as_vec<V>(*reinterpret_cast<const u32x4*>(&s_a[cur][nb * 16 + m][32 * j + 8 * kg]));
+        acc[nb] = M::mma(xo, ao, acc[nb]);
       }
     }
     if (more) {
