@@ -101,7 +101,10 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(ShrinkParams p, i
   const int dlen = min(d_chunk, p.D - d0);
   if (dlen <= 0) continue;
 
-  if (tid < kGroup) s_tok[tid] = tid < cnt ? load_token(p.rec, p.T, L.perm, it.p0 + sub * kGroup + tid) : 0;
+  if (tid < kGroup) {
+    const int t = item_token(p.rec, p.T, p.S, use_tiles != 0, item_id, sub * kGroup + tid, it.cnt);
+    s_tok[tid] = t < 0 ? 0 : t;
+  }
   __syncthreads();
 
   // stage the group's x rows for [d0, d0 + dlen): every load is issued before
@@ -250,7 +253,10 @@ __global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(ExpandParams p, i
   const int r = slot_rank(p.ranks, s, p.r_max);
   if (r == 0) continue;
 
-  if (tid < kGroup) s_tok[tid] = tid < cnt ? load_token(p.rec, p.T, L.perm, it.p0 + sub * kGroup + tid) : 0;
+  if (tid < kGroup) {
+    const int t = item_token(p.rec, p.T, p.S, use_tiles != 0, item_id, sub * kGroup + tid, it.cnt);
+    s_tok[tid] = t < 0 ? 0 : t;
+  }
   __syncthreads();
   const float* vb = p.v + (int64_t)slice * p.v_slice_stride;
   {

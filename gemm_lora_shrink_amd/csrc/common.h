@@ -28,10 +28,15 @@ enum InfoWord {
   kBuiltS = 7,
 };
 
-// One work item: tokens perm[p0 .. p0 + cnt) all have slot `slot`.
+// One work item: tokens perm[p0 .. p0 + cnt) all have slot `slot`.  In the
+// record an item is this header followed by its token indices inline (padded
+// to the list's item capacity with -1), so a kernel gets the header and the
+// tokens in one memory round trip.
 struct Item {
   int p0, cnt, slot, seg;
 };
+constexpr int kGroupItemWords = 4 + kGroup;  // 20
+constexpr int kTileItemWords = 4 + kTile;    // 68
 
 struct SegLayout {
   int64_t perm, seg_slot, seg_start, groups, tiles, words;
@@ -48,9 +53,9 @@ __host__ __device__ inline SegLayout seg_layout(int64_t T, int64_t S) {
   L.groups = (L.seg_start + S + 1 + 3) & ~int64_t(3);  // 16-byte aligned items
   int64_t minST = S < T ? S : T;
   L.cap_groups = ceil_div(T, kGroup) + minST;
-  L.tiles = L.groups + 4 * L.cap_groups;
+  L.tiles = L.groups + kGroupItemWords * L.cap_groups;
   L.cap_tiles = ceil_div(T, kTile) + minST;
-  L.words = L.tiles + 4 * L.cap_tiles;
+  L.words = L.tiles + kTileItemWords * L.cap_tiles;
   return L;
 }
 
@@ -208,12 +213,6 @@ struct ExpandParams {
   int32_t S, r_max, n_slices, T;
 };
 
-// Token index stored at perm position `pos`, clamped into [0, T).
-__device__ inline int load_token(const int32_t* rec, int T, int64_t perm_off, int pos) {
-  const int t = rec[perm_off + pos];
-  return t < 0 ? 0 : (t >= T ? T - 1 : t);
-}
-
 // Persistent work loops.  A launch has a fixed number of workgroups (a
 // multiple of 8, sized to what the chip holds at once) and walks a work list
 // whose length is only known on the device.  The hardware hands workgroup b
@@ -245,12 +244,25 @@ __device__ inline int record_items(const int32_t* rec, int T, int S, bool tiles)
   return (n < 0 || n > (tiles ? L.cap_tiles : L.cap_groups)) ? 0 : n;
 }
 
-// Item `i` (< record_items) of a list, with its fields checked against the sizes.
-__device__ inline bool read_item(const int32_t* rec, int T, int S, bool tiles, int64_t i, Item& it) {
+// Word pointer to item `i` of a list (header, then inline tokens).
+__device__ inline const int32_t* item_ptr(const int32_t* rec, int T, int S, bool tiles, int64_t i) {
   const SegLayout L = seg_layout(T, S);
-  it = reinterpret_cast<const Item*>(rec + (tiles ? L.tiles : L.groups))[i];
+  return rec + (tiles ? L.tiles + i * kTileItemWords : L.groups + i * kGroupItemWords);
+}
+
+// Header of item `i` (< record_items) of a list, with its fields checked
+// against the sizes.
+__device__ inline bool read_item(const int32_t* rec, int T, int S, bool tiles, int64_t i, Item& it) {
+  it = *reinterpret_cast<const Item*>(item_ptr(rec, T, S, tiles, i));
   const int cap = tiles ? kTile : kGroup;
   return it.slot >= 0 && it.slot < S && it.p0 >= 0 && it.cnt > 0 && it.cnt <= cap && it.p0 + it.cnt <= T;
+}
+
+// Token k of item `i`, clamped into [0, T); -1 when k is past the item's count.
+__device__ inline int item_token(const int32_t* rec, int T, int S, bool tiles, int64_t i, int k, int cnt) {
+  const int t = item_ptr(rec, T, S, tiles, i)[4 + k];
+  if (k >= cnt) return -1;
+  return t < 0 ? 0 : (t >= T ? T - 1 : t);
 }
 
 __device__ inline int slot_rank(const int32_t* ranks, int s, int r_max) {

@@ -13,7 +13,11 @@
 //   4. a stable scatter of the tokens into perm, 1024 tokens per chunk: inside a
 //      wave, lanes holding the same slot find each other with ballots; across
 //      the 16 waves a per-(wave, slot) count table gives each wave its offset in
-//      wave order.  No atomics touch the order.
+//      wave order.  No atomics touch the order;
+//   5. the work items, each followed by its token indices, read back from an
+//      LDS mirror of perm (from global memory past 8192 tokens).
+// The first 8192 slot indices are loaded once, all at the same time, and kept
+// in registers.
 #include "common.h"
 
 namespace lora {
@@ -74,6 +78,58 @@ __device__ inline int upper_slot(const int* arr, int n, int key) {
   return lo;
 }
 
+constexpr int kRegChunks = 8;                  // idx chunks held in registers (T <= 8192)
+constexpr int kLdsPerm = kRegChunks * kThreads;  // perm positions mirrored in LDS
+
+// Stable placement of one chunk of 1024 tokens (t = c0 + tid, slot s).
+__device__ inline void scatter_chunk(int t, int s, int S, int32_t* __restrict__ perm, int* s_perm, int* s_run,
+                                     uint8_t (*s_wtab)[LORA_MAX_SLOTS], int* s_leader_base) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const bool valid = s >= 0 && s < S;
+  // lanes of this wave with the same slot
+  uint64_t remaining = __ballot(valid);
+  uint64_t peers = 0;
+  while (remaining) {
+    const int leader = __builtin_ctzll(remaining);
+    const int ls = __shfl(s, leader, 64);
+    const uint64_t m = __ballot(valid && s == ls);
+    if (valid && s == ls) peers = m;
+    remaining &= ~m;
+  }
+  const bool is_leader = valid && (peers & lt_mask) == 0;
+  const int wcount = __popcll(peers);
+  if (is_leader) s_wtab[wave][s] = (uint8_t)wcount;
+  __syncthreads();
+  int base = 0;
+  bool last_wave = false;
+  if (is_leader) {
+    int pre = 0, post = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = s_wtab[w][s];
+      if (w < wave) pre += c;
+      if (w > wave) post += c;
+    }
+    base = s_run[s] + pre;
+    last_wave = (post == 0);
+    s_leader_base[tid] = base;
+  }
+  __syncthreads();
+  if (valid) {
+    const int pos = s_leader_base[(wave << 6) + __builtin_ctzll(peers)] + __popcll(peers & lt_mask);
+    perm[pos] = t;
+    if (pos < kLdsPerm) s_perm[pos] = t;
+  }
+  if (is_leader) {
+    s_wtab[wave][s] = 0;
+    if (last_wave) s_run[s] = base + wcount;
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t* __restrict__ idx, int T, int S,
                                                                   int mode, int32_t* __restrict__ rec) {
   __shared__ int s_count[LORA_MAX_SLOTS];
@@ -84,13 +140,23 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   __shared__ int s_tofs[LORA_MAX_SLOTS + 1];
   __shared__ uint8_t s_wtab[kWaves][LORA_MAX_SLOTS];
   __shared__ int s_leader_base[kThreads];
+  __shared__ int s_perm[kLdsPerm];
   __shared__ int4 s_wave_sums[kWaves + 1];
   __shared__ int s_bad, s_maxlen;
 
   const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = tid >> 6;
   const SegLayout L = seg_layout(T, S);
+  int32_t* perm = rec + L.perm;
+
+  // the first 8192 slot indices stay in registers; all loads are issued at once
+  int my_idx[kRegChunks];
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int t = c * kThreads + tid;
+    const int32_t* src = t < T ? idx + t : reinterpret_cast<const int32_t*>(g_zero16);  // idx may be null when T = 0
+    my_idx[c] = *src;
+    if (t >= T) my_idx[c] = -1;
+  }
 
   for (int s = tid; s < S; s += kThreads) {
     s_count[s] = 0;
@@ -105,8 +171,14 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
 
   // 1. counts
   int bad = 0;
-  for (int t = tid; t < T; t += kThreads) {
-    int s = idx[t];
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int s = my_idx[c];
+    if (s >= 0 && s < S) atomicAdd(&s_count[s], 1);
+    else if (s != -1) bad = 1;
+  }
+  for (int t = kRegChunks * kThreads + tid; t < T; t += kThreads) {
+    const int s = idx[t];
     if (s >= 0 && s < S) atomicAdd(&s_count[s], 1);
     else if (s != -1) bad = 1;
   }
@@ -117,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   const int n = tid < S ? s_count[tid] : 0;
   int ng = 0, nt = 0;
   if (n > 0) {
-    bool to_tiles = (mode == LORA_MODE_SGMV) || (mode == LORA_MODE_AUTO && n >= kSgmvMinTokens);
+    const bool to_tiles = (mode == LORA_MODE_SGMV) || (mode == LORA_MODE_AUTO && n >= kSgmvMinTokens);
     if (to_tiles) nt = (int)ceil_div(n, kTile);
     else ng = (int)ceil_div(n, kGroup);
     atomicMax(&s_maxlen, n);
@@ -156,75 +228,50 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
     rec[kBuiltS] = S;
     for (int w = 8; w < kInfoWords; ++w) rec[w] = 0;
   }
-  Item* groups = reinterpret_cast<Item*>(rec + L.groups);
-  Item* tiles = reinterpret_cast<Item*>(rec + L.tiles);
-  for (int i = tid; i < n_groups; i += kThreads) {
-    int s = upper_slot(s_gofs, S, i);
-    int g = i - s_gofs[s];
-    Item it;
-    it.p0 = s_start[s] + g * kGroup;
-    it.cnt = min(kGroup, s_count[s] - g * kGroup);
-    it.slot = s;
-    it.seg = s_seg[s];
-    groups[i] = it;
-  }
-  for (int i = tid; i < n_tiles; i += kThreads) {
-    int s = upper_slot(s_tofs, S, i);
-    int g = i - s_tofs[s];
-    Item it;
-    it.p0 = s_start[s] + g * kTile;
-    it.cnt = min(kTile, s_count[s] - g * kTile);
-    it.slot = s;
-    it.seg = s_seg[s];
-    tiles[i] = it;
-  }
 
-  // 4. stable scatter into perm
-  int32_t* perm = rec + L.perm;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < T; c0 += kThreads) {
-    const int t = c0 + tid;
-    const int s = t < T ? idx[t] : -1;
-    const bool valid = s >= 0 && s < S;
-    // lanes of this wave with the same slot
-    uint64_t remaining = __ballot(valid);
-    uint64_t peers = 0;
-    while (remaining) {
-      const int leader = __builtin_ctzll(remaining);
-      const int ls = __shfl(s, leader, 64);
-      const uint64_t m = __ballot(valid && s == ls);
-      if (valid && s == ls) peers = m;
-      remaining &= ~m;
-    }
-    const bool is_leader = valid && (peers & lt_mask) == 0;
-    const int wcount = __popcll(peers);
-    if (is_leader) s_wtab[wave][s] = (uint8_t)wcount;
-    __syncthreads();
-    int base = 0;
-    bool last_wave = false;
-    if (is_leader) {
-      int pre = 0, post = 0;
+  // 4. stable scatter into perm (and its LDS mirror)
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        int c = s_wtab[w][s];
-        if (w < wave) pre += c;
-        if (w > wave) post += c;
-      }
-      base = s_run[s] + pre;
-      last_wave = (post == 0);
-      s_leader_base[tid] = base;
-    }
-    __syncthreads();
-    if (valid) {
-      const int leader_tid = (wave << 6) + __builtin_ctzll(peers);
-      const int b = s_leader_base[leader_tid];
-      perm[b + __popcll(peers & lt_mask)] = t;
-    }
-    if (is_leader) {
-      s_wtab[wave][s] = 0;
-      if (last_wave) s_run[s] = base + wcount;
-    }
-    __syncthreads();
+  for (int c = 0; c < kRegChunks; ++c)
+    if (c * kThreads < T) scatter_chunk(c * kThreads + tid, my_idx[c], S, perm, s_perm, s_run, s_wtab, s_leader_base);
+  for (int c0 = kRegChunks * kThreads; c0 < T; c0 += kThreads) {
+    const int t = c0 + tid;
+    scatter_chunk(t, t < T ? idx[t] : -1, S, perm, s_perm, s_run, s_wtab, s_leader_base);
+  }
+  if (T > kLdsPerm) __threadfence();  // the items below read perm back from global memory
+  __syncthreads();
+
+  // 5. work items: header, then the item's tokens inline (-1 past the count)
+  auto perm_at = [&](int pos) -> int {
+    if (pos < kLdsPerm) return s_perm[pos];
+    return __hip_atomic_load(perm + pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  for (int e = tid; e < n_groups * kGroupItemWords; e += kThreads) {
+    const int i = e / kGroupItemWords, wd = e - i * kGroupItemWords;
+    const int s = upper_slot(s_gofs, S, i);
+    const int g = i - s_gofs[s];
+    const int p0 = s_start[s] + g * kGroup;
+    const int cnt = min(kGroup, s_count[s] - g * kGroup);
+    int v;
+    if (wd == 0) v = p0;
+    else if (wd == 1) v = cnt;
+    else if (wd == 2) v = s;
+    else if (wd == 3) v = s_seg[s];
+    else v = (wd - 4 < cnt) ? perm_at(p0 + wd - 4) : -1;
+    rec[L.groups + e] = v;
+  }
+  for (int e = tid; e < n_tiles * kTileItemWords; e += kThreads) {
+    const int i = e / kTileItemWords, wd = e - i * kTileItemWords;
+    const int s = upper_slot(s_tofs, S, i);
+    const int g = i - s_tofs[s];
+    const int p0 = s_start[s] + g * kTile;
+    const int cnt = min(kTile, s_count[s] - g * kTile);
+    int v;
+    if (wd == 0) v = p0;
+    else if (wd == 1) v = cnt;
+    else if (wd == 2) v = s;
+    else if (wd == 3) v = s_seg[s];
+    else v = (wd - 4 < cnt) ? perm_at(p0 + wd - 4) : -1;
+    rec[L.tiles + e] = v;
   }
 }
 

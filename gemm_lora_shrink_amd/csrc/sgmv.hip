@@ -87,118 +87,47 @@ constexpr int kSubs = kTile / 16;                              // 16-token sub-b
 constexpr int kTrRow = kExpandColsPerWave + 4;                 // padded fp32 LDS row
 constexpr int kVRow = LORA_MAX_RANK + 8;                       // padded 16-bit LDS row of v
 
-template <typename Elem>
-__global__ __launch_bounds__(kThreads, 4) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles,
-                                                               int n_ct) {
+// The column tiles [ct_begin, ct_end) of one unit: NSUB 16-token sub-blocks
+// (1 for a gather group, up to 4 for a tile; sub-blocks past the item's
+// tokens hold no token and are skipped by their -1 entries).
+template <typename Elem, int NSUB>
+__device__ inline void expand_columns(const ExpandParams& p, const int* s_tok, const float* s_unscale,
+                                      const Elem (*s_vhi)[kVRow], const Elem (*s_vlo)[kVRow],
+                                      float (*s_tr)[16][kTrRow], int slice, int s, int r, int out, int ct_begin,
+                                      int ct_end) {
   using M = Mfma<Elem>;
   using V = typename M::vec;
   using Tr = Traits<Elem>;
-  __shared__ int s_tok[kTile];
-  __shared__ float s_unscale[kTile];
-  __shared__ __attribute__((aligned(16))) Elem s_vhi[kTile][kVRow];
-  __shared__ __attribute__((aligned(16))) Elem s_vlo[kTile][kVRow];
-  __shared__ __attribute__((aligned(16))) float s_tr[4][16][kTrRow];
-
-  const SegLayout L = seg_layout(p.T, p.S);
-  const int n_g = use_groups ? record_items(p.rec, p.T, p.S, false) : 0;
-  const int n_t = use_tiles ? record_items(p.rec, p.T, p.S, true) : 0;
-  const int64_t n_items = (int64_t)n_g + n_t;
-  // column tiles per unit: enough units to give every workgroup about two
-  const int64_t tile_slots = n_items * n_ct * p.n_slices;
-  int run = (int)(tile_slots / (2 * (int64_t)gridDim.x));
-  run = run < 1 ? 1 : (run > n_ct ? n_ct : run);
-  const int n_runs = (n_ct + run - 1) / run;
-  // unit order: item fastest, then column run, then slice
-  const WorkRange R = xcd_work_range(n_items * n_runs * p.n_slices);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;
   const int yr = lane >> 3, yc = (lane & 7) * 8;
   const Elem* yzero = reinterpret_cast<const Elem*>(g_zero16);
-
-  for (int64_t w = R.begin; w < R.end; w += R.step) {
-  const int64_t item = w % n_items;
-  const int64_t rest = w / n_items;
-  const int cr = (int)(rest % n_runs);
-  const int slice = (int)(rest / n_runs);
-  const bool tiles = item >= n_g;
-  Item it;
-  if (!read_item(p.rec, p.T, p.S, tiles, tiles ? item - n_g : item, it)) continue;
-  const int out = (int)p.out_size[slice];
-  const int ct_begin = cr * run;
-  const int ct_end = min(ct_begin + run, (int)ceil_div(out, kExpandColsPerWG));
-  if (ct_begin >= ct_end) continue;
-  const int s = it.slot;
-  const int r = slot_rank(p.ranks, s, p.r_max);
-  if (r == 0) continue;
   const int nks = r > 32 ? 2 : 1;  // 32-wide rank steps
-  const int n_sub = (it.cnt + 15) >> 4;
-
-  // token list and the item's v rows as hi + lo (thread: token tid / 4,
-  // ranks 16 (tid % 4) .. +15)
-  {
-    const int tt = tid >> 2, kq = (tid & 3) * 16;
-    const int tok = tt < it.cnt ? load_token(p.rec, p.T, L.perm, it.p0 + tt) : -1;
-    if ((tid & 3) == 0) s_tok[tt] = tok;
-    const float* src = p.v + (int64_t)slice * p.v_slice_stride + (int64_t)(tok >= 0 ? tok : 0) * p.r_max + kq;
-    float vv[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool ok = tok >= 0 && kq + 4 * q < p.r_max;
-      const f32x4 f = ldf4_or0(src + (ok ? 4 * q : 0), ok);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vv[4 * q + e] = (kq + 4 * q + e < r) ? f[e] : 0.f;
-    }
-    float unscale = 1.0f;
-    if constexpr (Tr::kDtype == LORA_F16) {
-      // scale the token's row by a power of two so that |v| < 2
-      float mx = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(vv[e]));
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-      if (mx > 0.f) {
-        int ex;
-        frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
-        const float sc = ldexpf(1.0f, 1 - ex);
-        unscale = ldexpf(1.0f, ex - 1);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) vv[e] *= sc;
-      }
-    }
-    if ((tid & 3) == 0) s_unscale[tt] = unscale;
-    V hi0, hi1, lo0, lo1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const Elem h0 = static_cast<Elem>(vv[e]), h1 = static_cast<Elem>(vv[8 + e]);
-      hi0[e] = h0;
-      hi1[e] = h1;
-      lo0[e] = static_cast<Elem>(vv[e] - static_cast<float>(h0));
-      lo1[e] = static_cast<Elem>(vv[8 + e] - static_cast<float>(h1));
-    }
-    *reinterpret_cast<V*>(&s_vhi[tt][kq]) = hi0;
-    *reinterpret_cast<V*>(&s_vhi[tt][kq + 8]) = hi1;
-    *reinterpret_cast<V*>(&s_vlo[tt][kq]) = lo0;
-    *reinterpret_cast<V*>(&s_vlo[tt][kq + 8]) = lo1;
-  }
-  __syncthreads();
-
+  const int n_sub = NSUB;
   const Elem* Bs = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max;
   Elem* ybase = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + yc;
-  for (int ct = ct_begin; ct < ct_end; ++ct) {
+  // y of every sub-block of column tile `ct`, lane-contiguous (zeros past the end)
+  auto load_y = [&](int ct, u32x4 (&dst)[NSUB][2]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
-    const bool ycol_ok = jw + yc < out;  // out is a multiple of 8
-    // y of every sub-block, first
-    u32x4 yold[kSubs][2];
+    const bool ycol_ok = ct < ct_end && jw + yc < out;  // out is a multiple of 8
 #pragma unroll
-    for (int sb = 0; sb < kSubs; ++sb)
+    for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int t = sb < n_sub ? s_tok[sb * 16 + h * 8 + yr] : -1;
         const bool ok = ycol_ok && t >= 0;
-        yold[sb][h] = ld16_or0(ok ? ybase + jw + (int64_t)t * p.ldy : yzero, ok);
+        dst[sb][h] = ld16_or0(ok ? ybase + jw + (int64_t)t * p.ldy : yzero, ok);
       }
-    // A operand: this wave's 64 B rows (4 blocks x 16), both rank steps
+  };
+  u32x4 yold[NSUB][2];
+  load_y(ct_begin, yold);
+  for (int ct = ct_begin; ct < ct_end; ++ct) {
+    const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
+    const bool ycol_ok = jw + yc < out;  // out is a multiple of 8
+    // A operand: this wave's 64 B rows (4 blocks x 16), both rank steps.  They
+    // are requested before the next tile's y, so that waiting for them never
+    // waits for that prefetch (loads complete in order).
     V bop[4][2];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
@@ -206,12 +135,14 @@ __global__ __launch_bounds__(kThreads, 4) void mfma_expand_kernel(ExpandParams p
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int k0 = ks * 32 + kg * 8;
-        const bool ok = ks < nks && row < out && k0 < p.r_max;
+        const bool ok = ks < nks && row < out && k0 < r;  // rank columns past the slot's rank are not read
         bop[cb][ks] = as_vec<V>(mask_tail16(ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok), k0, r));
       }
     }
+    u32x4 ynext[NSUB][2];
+    load_y(ct + 1, ynext);
 #pragma unroll
-    for (int sb = 0; sb < kSubs; ++sb) {
+    for (int sb = 0; sb < NSUB; ++sb) {
       if (sb >= n_sub) break;
       // B operand: v[tok 16 sb + n][32 ks + 8 kg .. +7], hi and lo
       V vhi[2], vlo[2];
@@ -261,7 +192,254 @@ __global__ __launch_bounds__(kThreads, 4) void mfma_expand_kernel(ExpandParams p
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      yold[sb][0] = ynext[sb][0];
+      yold[sb][1] = ynext[sb][1];
+    }
   }
+}
+
+// A gather group (at most 16 tokens) needs no shared staging: each wave loads
+// its own v operands, so a unit costs two memory round trips -- the item
+// (header and tokens), then its y, B and v together -- and no workgroup barrier.
+template <typename Elem>
+__device__ inline void expand_group_direct(const ExpandParams& p, const int32_t* ip, const Item& it,
+                                           float (*s_tr)[16][kTrRow], int slice, int s, int r, int out,
+                                           int ct_begin, int ct_end) {
+  using M = Mfma<Elem>;
+  using V = typename M::vec;
+  using Tr = Traits<Elem>;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, kg = lane >> 4;
+  const int yr = lane >> 3, yc = (lane & 7) * 8;
+  const int nks = r > 32 ? 2 : 1;
+  const bool ragged_rank = (r & 7) != 0;
+  auto tok_at = [&](int k) -> int {
+    const int t = ip[4 + k];
+    return k < it.cnt ? (t < 0 ? 0 : (t >= p.T ? p.T - 1 : t)) : -1;
+  };
+  const int tok_n = tok_at(n);
+  const int ytok0 = tok_at(yr), ytok1 = tok_at(yr + 8);
+  const Elem* Bs = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max;
+  const Elem* yzero = reinterpret_cast<const Elem*>(g_zero16);
+  Elem* ybase = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + yc;
+  const float* vrow = p.v + (int64_t)slice * p.v_slice_stride + (int64_t)(tok_n >= 0 ? tok_n : 0) * p.r_max;
+
+  for (int ct = ct_begin; ct < ct_end; ++ct) {
+    const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
+    const bool ycol_ok = jw + yc < out;  // out is a multiple of 8
+    // y, B and (first tile) v requests go out together
+    u32x4 yold[2];
+    yold[0] = ld16_or0(ycol_ok && ytok0 >= 0 ? ybase + jw + (int64_t)ytok0 * p.ldy : yzero, ycol_ok && ytok0 >= 0);
+    yold[1] = ld16_or0(ycol_ok && ytok1 >= 0 ? ybase + jw + (int64_t)ytok1 * p.ldy : yzero, ycol_ok && ytok1 >= 0);
+    u32x4 braw[4][2];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int row = jw + cb * 16 + n;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int k0 = ks * 32 + kg * 8;
+        const bool ok = ks < nks && row < out && k0 < r;
+        braw[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok);
+      }
+    }
+    f32x4 vraw[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int k0 = ks * 32 + kg * 8;
+      const bool ok = tok_n >= 0 && ks < nks && k0 < r;
+      vraw[ks][0] = ldf4_or0(vrow + (ok ? k0 : 0), ok);
+      vraw[ks][1] = ldf4_or0(vrow + (ok ? k0 + 4 : 0), ok);
+    }
+    V bop[4][2];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        bop[cb][ks] = as_vec<V>(ragged_rank ? mask_tail16(braw[cb][ks], ks * 32 + kg * 8, r) : braw[cb][ks]);
+    float vv[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int k0 = ks * 32 + kg * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vv[ks][i] = (k0 + i < r) ? vraw[ks][0][i] : 0.f;
+        vv[ks][4 + i] = (k0 + 4 + i < r) ? vraw[ks][1][i] : 0.f;
+      }
+    }
+    float unscale = 1.0f;
+    if constexpr (Tr::kDtype == LORA_F16) {
+      float mx = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(vv[ks][i]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (mx > 0.f) {
+        int ex;
+        frexpf(mx, &ex);
+        const float sc = ldexpf(1.0f, 1 - ex);
+        unscale = ldexpf(1.0f, ex - 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) vv[ks][i] *= sc;
+      }
+    }
+    V vhi[2], vlo[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const Elem h = static_cast<Elem>(vv[ks][i]);
+        vhi[ks][i] = h;
+        vlo[ks][i] = static_cast<Elem>(vv[ks][i] - static_cast<float>(h));
+      }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc = M::mma(bop[cb][0], vhi[0], acc);
+      acc = M::mma(bop[cb][0], vlo[0], acc);
+      if (nks > 1) {
+        acc = M::mma(bop[cb][1], vhi[1], acc);
+        acc = M::mma(bop[cb][1], vlo[1], acc);
+      }
+      if constexpr (Tr::kDtype == LORA_F16) acc *= unscale;
+      *reinterpret_cast<f32x4*>(&s_tr[wave][n][cb * 16 + kg * 4]) = acc;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = h ? ytok1 : ytok0;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&s_tr[wave][h * 8 + yr][yc]);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&s_tr[wave][h * 8 + yr][yc + 4]);
+      if (ycol_ok && t >= 0) {
+        const float add[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t wd = yold[h][q];
+          const float y0 = Tr::elem_to_float(wd & 0xffffu) + add[2 * q];
+          const float y1 = Tr::elem_to_float(wd >> 16) + add[2 * q + 1];
+          if constexpr (Tr::kDtype == LORA_BF16) o[q] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
+          else o[q] = float_to_f16_bits(y0) | (float_to_f16_bits(y1) << 16);
+        }
+        *reinterpret_cast<u32x4*>(ybase + jw + (int64_t)t * p.ldy) = o;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads, 3) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles,
+                                                               int n_ct) {
+  using M = Mfma<Elem>;
+  using V = typename M::vec;
+  using Tr = Traits<Elem>;
+  __shared__ int s_tok[kTile];
+  __shared__ float s_unscale[kTile];
+  __shared__ __attribute__((aligned(16))) Elem s_vhi[kTile][kVRow];
+  __shared__ __attribute__((aligned(16))) Elem s_vlo[kTile][kVRow];
+  __shared__ __attribute__((aligned(16))) float s_tr[4][16][kTrRow];
+
+  const SegLayout L = seg_layout(p.T, p.S);
+  const int n_g = use_groups ? record_items(p.rec, p.T, p.S, false) : 0;
+  const int n_t = use_tiles ? record_items(p.rec, p.T, p.S, true) : 0;
+  const int64_t n_items = (int64_t)n_g + n_t;
+  // column tiles per unit: enough units to give every workgroup about two
+  const int64_t tile_slots = n_items * n_ct * p.n_slices;
+  int run = (int)(tile_slots / (2 * (int64_t)gridDim.x));
+  run = run < 1 ? 1 : (run > n_ct ? n_ct : run);
+  const int n_runs = (n_ct + run - 1) / run;
+  // unit order: item fastest, then column run, then slice
+  const WorkRange R = xcd_work_range(n_items * n_runs * p.n_slices);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, kg = lane >> 4;
+  const int yr = lane >> 3, yc = (lane & 7) * 8;
+  const Elem* yzero = reinterpret_cast<const Elem*>(g_zero16);
+
+  for (int64_t w = R.begin; w < R.end; w += R.step) {
+  const int64_t item = w % n_items;
+  const int64_t rest = w / n_items;
+  const int cr = (int)(rest % n_runs);
+  const int slice = (int)(rest / n_runs);
+  const bool tiles = item >= n_g;
+  Item it;
+  if (!read_item(p.rec, p.T, p.S, tiles, tiles ? item - n_g : item, it)) continue;
+  const int out = (int)p.out_size[slice];
+  const int ct_begin = cr * run;
+  const int ct_end = min(ct_begin + run, (int)ceil_div(out, kExpandColsPerWG));
+  if (ct_begin >= ct_end) continue;
+  const int s = it.slot;
+  const int r = slot_rank(p.ranks, s, p.r_max);
+  if (r == 0) continue;
+  if (it.cnt <= 16) {
+    // uniform per unit; this path uses only wave-private LDS
+    expand_group_direct<Elem>(p, item_ptr(p.rec, p.T, p.S, tiles, tiles ? item - n_g : item), it, s_tr, slice,
+                              s, r, out, ct_begin, ct_end);
+    continue;
+  }
+  const int n_sub = (it.cnt + 15) >> 4;
+
+  // token list and the item's v rows as hi + lo (thread: token tid / 4,
+  // ranks 16 (tid % 4) .. +15)
+  {
+    const int tt = tid >> 2, kq = (tid & 3) * 16;
+    const int tok = item_token(p.rec, p.T, p.S, tiles, tiles ? item - n_g : item, tt, it.cnt);
+    if ((tid & 3) == 0) s_tok[tt] = tok;
+    const float* src = p.v + (int64_t)slice * p.v_slice_stride + (int64_t)(tok >= 0 ? tok : 0) * p.r_max + kq;
+    float vv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = tok >= 0 && kq + 4 * q < p.r_max;
+      const f32x4 f = ldf4_or0(src + (ok ? 4 * q : 0), ok);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[4 * q + e] = (kq + 4 * q + e < r) ? f[e] : 0.f;
+    }
+    float unscale = 1.0f;
+    if constexpr (Tr::kDtype == LORA_F16) {
+      // scale the token's row by a power of two so that |v| < 2
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(vv[e]));
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+      if (mx > 0.f) {
+        int ex;
+        frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
+        const float sc = ldexpf(1.0f, 1 - ex);
+        unscale = ldexpf(1.0f, ex - 1);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vv[e] *= sc;
+      }
+    }
+    if ((tid & 3) == 0) s_unscale[tt] = unscale;
+    V hi0, hi1, lo0, lo1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const Elem h0 = static_cast<Elem>(vv[e]), h1 = static_cast<Elem>(vv[8 + e]);
+      hi0[e] = h0;
+      hi1[e] = h1;
+      lo0[e] = static_cast<Elem>(vv[e] - static_cast<float>(h0));
+      lo1[e] = static_cast<Elem>(vv[8 + e] - static_cast<float>(h1));
+    }
+    *reinterpret_cast<V*>(&s_vhi[tt][kq]) = hi0;
+    *reinterpret_cast<V*>(&s_vhi[tt][kq + 8]) = hi1;
+    *reinterpret_cast<V*>(&s_vlo[tt][kq]) = lo0;
+    *reinterpret_cast<V*>(&s_vlo[tt][kq + 8]) = lo1;
+  }
+  __syncthreads();
+
+  expand_columns<Elem, kSubs>(p, s_tok, s_unscale, s_vhi, s_vlo, s_tr, slice, s, r, out, ct_begin, ct_end);
   __syncthreads();  // the next unit rewrites s_tok and the v operands
   }
 }
@@ -296,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void mfma_shrink_kernel(ShrinkParams p) {
   const int r = slot_rank(p.ranks, s, p.r_max);
   if (r == 0) continue;
 
-  if (tid < kTile) s_tok[tid] = tid < it.cnt ? load_token(p.rec, p.T, L.perm, it.p0 + tid) : -1;
+  if (tid < kTile) s_tok[tid] = item_token(p.rec, p.T, p.S, true, tile, tid, it.cnt);
   __syncthreads();
 
   const int wave = tid >> 6, lane = tid & 63;

@@ -47,8 +47,9 @@ def test_segment_record_layout(T, S):
     assert off["groups"] >= off["seg_start"] + S + 1 and off["groups"] % 4 == 0
     cap_groups = -(-T // 16) + min(S, T)
     cap_tiles = -(-T // 64) + min(S, T)
-    assert off["tiles"] == off["groups"] + 4 * cap_groups
-    assert (off["tiles"] + 4 * cap_tiles) * 4 <= nbytes
+    # items: a 4-word header then the item's tokens inline (16 per group, 64 per tile)
+    assert off["tiles"] == off["groups"] + 20 * cap_groups
+    assert (off["tiles"] + 68 * cap_tiles) * 4 <= nbytes
 
 
 def test_bad_sizes_give_zero_bytes():

@@ -44,9 +44,14 @@ def check_record(idx, S, mode, label):
     thr = glsa.sgmv_min_tokens()
     covered = np.zeros(na, dtype=np.int32)
     for name, cap, n in (("groups", 16, info[4]), ("tiles", 64, info[5])):
-        items = rec[off[name]:off[name] + 4 * n].reshape(n, 4)
-        for p0, cnt, slot, segno in items:
+        words = 4 + cap
+        items = rec[off[name]:off[name] + words * n].reshape(n, words)
+        for row in items:
+            p0, cnt, slot, segno = (int(v) for v in row[:4])
             assert 1 <= cnt <= cap, label
+            # the item's tokens follow its header, then -1 padding
+            assert np.array_equal(row[4:4 + cnt], ref["perm"][p0:p0 + cnt]), label
+            assert np.all(row[4 + cnt:] == -1), label
             assert ref["seg_slot"][segno] == slot, label
             assert ref["seg_start"][segno] <= p0 and p0 + cnt <= ref["seg_start"][segno + 1], label
             covered[p0:p0 + cnt] += 1
@@ -96,8 +101,8 @@ def specified_words(rec, T, S):
         info, rec[off["perm"]:off["perm"] + info[0]],
         rec[off["seg_slot"]:off["seg_slot"] + info[1]],
         rec[off["seg_start"]:off["seg_start"] + info[1] + 1],
-        rec[off["groups"]:off["groups"] + 4 * info[4]],
-        rec[off["tiles"]:off["tiles"] + 4 * info[5]]])
+        rec[off["groups"]:off["groups"] + 20 * info[4]],
+        rec[off["tiles"]:off["tiles"] + 68 * info[5]]])
 
 
 def test_deterministic_over_repeats():
