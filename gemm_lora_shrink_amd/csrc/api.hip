@@ -55,6 +55,18 @@ bool gather_expand_on_valu() {
   return valu;
 }
 
+// Kernel used for the shrink of segmented tiles of 16-bit data.  By default the
+// one shrink launch covers them; LORA_MI355X_TILE_SHRINK=lds runs them in a
+// second launch whose workgroups share the slot's A chunk through LDS (kept for
+// comparison measurements).
+bool tile_shrink_on_lds() {
+  static const bool lds = [] {
+    const char* e = getenv("LORA_MI355X_TILE_SHRINK");
+    return e && strcmp(e, "lds") == 0;
+  }();
+  return lds;
+}
+
 lora_status check_common(int dt, int32_t T, int32_t n_slices, int32_t S, int32_t r_max, const void* seg) {
   if (!valid_dtype(dt)) return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", dt);
   if (T < 0) return fail(LORA_ERR_INVALID_ARG, "T = %d is negative", T);
@@ -184,6 +196,12 @@ LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, i
   if (D % vec || ldx % vec)
     return fail(LORA_ERR_UNSUPPORTED, "D and ldx must be multiples of %d elements for this dtype", vec);
   if (!x || !v) return fail(LORA_ERR_INVALID_ARG, "x or v is null");
+  // the shrink kernel addresses x and one slot's A rows with 32-bit byte offsets
+  const uint64_t esize = dt == LORA_F32 ? 4 : 2;
+  if (((uint64_t)(T - 1) * (uint64_t)ldx + (uint64_t)D) * esize > 0xFFFFFFFFull)
+    return fail(LORA_ERR_UNSUPPORTED, "x spans more than 4 GiB");
+  if ((uint64_t)r_max * (uint64_t)D * esize > 0xFFFFFFFFull)
+    return fail(LORA_ERR_UNSUPPORTED, "one slot's A rows span more than 4 GiB");
   if (!aligned16(x) || !aligned16(v)) return fail(LORA_ERR_UNSUPPORTED, "x and v must be 16-byte aligned");
   if (!A) return fail(LORA_ERR_INVALID_ARG, "A pointer array is null");
   ShrinkParams p = {};
@@ -207,13 +225,15 @@ LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, i
   p.n_slices = n_slices;
   p.T = T;
 
-  hipError_t e = launch_fill_zero(v, (int64_t)n_slices * T * r_max, stream);
-  if (e != hipSuccess) return hip_fail(e, "clear of v");
-  e = launch_bgmv_shrink(dt, p, /*tiles=*/false, stream);
-  if (e != hipSuccess) return hip_fail(e, "gather shrink launch");
-  if (dt == LORA_F32) e = launch_bgmv_shrink(dt, p, /*tiles=*/true, stream);
-  else e = launch_sgmv_shrink(dt, p, stream);
-  if (e != hipSuccess) return hip_fail(e, "segmented shrink launch");
+  // v is written in full by the shrink launch (rows of tokens without an
+  // adapter are cleared by it), so nothing is cleared beforehand
+  const bool split_tiles = dt != LORA_F32 && tile_shrink_on_lds();
+  hipError_t e = launch_shrink(dt, p, /*groups=*/true, /*tiles=*/!split_tiles, stream);
+  if (e != hipSuccess) return hip_fail(e, "shrink launch");
+  if (split_tiles) {
+    e = launch_sgmv_shrink(dt, p, stream);
+    if (e != hipSuccess) return hip_fail(e, "segmented shrink launch");
+  }
   return LORA_OK;
 }
 

@@ -279,9 +279,15 @@ int persistent_grid(const void* kernel, int block, size_t dyn_lds, int64_t max_u
 // Host-side launchers (defined in the .hip files).
 hipError_t launch_build_segments(const int32_t* idx, int32_t T, int32_t S, int32_t mode, int32_t* rec,
                                  hipStream_t stream);
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
-hipError_t launch_bgmv_shrink(lora_dtype dt, const ShrinkParams& p, bool tiles, hipStream_t stream);
+// Shrink of every work item of the record (the gather groups and/or the
+// segmented tiles) plus the clearing of the rows of tokens without an adapter,
+// in one launch.
+hipError_t launch_shrink(lora_dtype dt, const ShrinkParams& p, bool groups, bool tiles, hipStream_t stream);
+// v[0 .. n) = 0
+hipError_t launch_fill_zero(float* v, int64_t n, hipStream_t stream);
 hipError_t launch_bgmv_expand(lora_dtype dt, const ExpandParams& p, bool tiles, hipStream_t stream);
+// Shrink of the segmented tiles with the slot's A chunk shared through LDS
+// (16-bit types only).
 hipError_t launch_sgmv_shrink(lora_dtype dt, const ShrinkParams& p, hipStream_t stream);
 // Matrix-core expand over the gather groups and/or the segmented tiles, in one
 // launch (16-bit types only).

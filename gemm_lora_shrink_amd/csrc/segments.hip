@@ -13,7 +13,9 @@
 //   4. a stable scatter of the tokens into perm, 1024 tokens per chunk: inside a
 //      wave, lanes holding the same slot find each other with ballots; across
 //      the 16 waves a per-(wave, slot) count table gives each wave its offset in
-//      wave order.  No atomics touch the order;
+//      wave order.  No atomics touch the order.  Tokens without a valid slot
+//      are placed as if they had slot S, after all active tokens, so perm ends
+//      with them in ascending order (the shrink clears their v rows);
 //   5. the work items, each followed by its token indices, read back from an
 //      LDS mirror of perm (from global memory past 8192 tokens).
 // The first 8192 slot indices are loaded once, all at the same time, and kept
@@ -81,15 +83,18 @@ __device__ inline int upper_slot(const int* arr, int n, int key) {
 constexpr int kRegChunks = 8;                  // idx chunks held in registers (T <= 8192)
 constexpr int kLdsPerm = kRegChunks * kThreads;  // perm positions mirrored in LDS
 
-// Stable placement of one chunk of 1024 tokens (t = c0 + tid, slot s).
-__device__ inline void scatter_chunk(int t, int s, int S, int32_t* __restrict__ perm, int* s_perm, int* s_run,
-                                     uint8_t (*s_wtab)[LORA_MAX_SLOTS], int* s_leader_base) {
+// Stable placement of one chunk of 1024 tokens (t = c0 + tid, slot index s).
+// A token whose s is not a valid slot takes key S: those tokens follow every
+// active token in perm.  Lanes with t >= T place nothing.
+__device__ inline void scatter_chunk(int t, int s, int T, int S, int32_t* __restrict__ perm, int* s_perm, int* s_run,
+                                     uint8_t (*s_wtab)[LORA_MAX_SLOTS + 1], int* s_leader_base) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const bool valid = s >= 0 && s < S;
-  // lanes of this wave with the same slot
+  const bool valid = t < T;
+  s = (s >= 0 && s < S) ? s : S;
+  // lanes of this wave with the same key
   uint64_t remaining = __ballot(valid);
   uint64_t peers = 0;
   while (remaining) {
@@ -134,11 +139,11 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
                                                                   int mode, int32_t* __restrict__ rec) {
   __shared__ int s_count[LORA_MAX_SLOTS];
   __shared__ int s_start[LORA_MAX_SLOTS];
-  __shared__ int s_run[LORA_MAX_SLOTS];
+  __shared__ int s_run[LORA_MAX_SLOTS + 1];  // [S]: the tokens without a slot
   __shared__ int s_seg[LORA_MAX_SLOTS];
   __shared__ int s_gofs[LORA_MAX_SLOTS + 1];
   __shared__ int s_tofs[LORA_MAX_SLOTS + 1];
-  __shared__ uint8_t s_wtab[kWaves][LORA_MAX_SLOTS];
+  __shared__ uint8_t s_wtab[kWaves][LORA_MAX_SLOTS + 1];
   __shared__ int s_leader_base[kThreads];
   __shared__ int s_perm[kLdsPerm];
   __shared__ int4 s_wave_sums[kWaves + 1];
@@ -158,8 +163,8 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
     if (t >= T) my_idx[c] = -1;
   }
 
-  for (int s = tid; s < S; s += kThreads) {
-    s_count[s] = 0;
+  for (int s = tid; s <= S; s += kThreads) {
+    if (s < S) s_count[s] = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) s_wtab[w][s] = 0;
   }
@@ -207,6 +212,7 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   if (tid == 0) {
     s_gofs[S] = tot.z;
     s_tofs[S] = tot.w;
+    s_run[S] = tot.x;  // tokens without a slot start after the active ones
   }
   const int num_active = tot.x, num_seg = tot.y, n_groups = tot.z, n_tiles = tot.w;
 
@@ -232,10 +238,11 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   // 4. stable scatter into perm (and its LDS mirror)
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c)
-    if (c * kThreads < T) scatter_chunk(c * kThreads + tid, my_idx[c], S, perm, s_perm, s_run, s_wtab, s_leader_base);
+    if (c * kThreads < T)
+      scatter_chunk(c * kThreads + tid, my_idx[c], T, S, perm, s_perm, s_run, s_wtab, s_leader_base);
   for (int c0 = kRegChunks * kThreads; c0 < T; c0 += kThreads) {
     const int t = c0 + tid;
-    scatter_chunk(t, t < T ? idx[t] : -1, S, perm, s_perm, s_run, s_wtab, s_leader_base);
+    scatter_chunk(t, t < T ? idx[t] : -1, T, S, perm, s_perm, s_run, s_wtab, s_leader_base);
   }
   if (T > kLdsPerm) __threadfence();  // the items below read perm back from global memory
   __syncthreads();

@@ -596,7 +596,7 @@ hipError_t launch_sgmv_shrink(lora_dtype dt, const ShrinkParams& p, hipStream_t 
   switch (dt) {
     case LORA_F16: return shrink_launch<half_t>(p, stream);
     case LORA_BF16: return shrink_launch<bf16_t>(p, stream);
-    default: return launch_bgmv_shrink(dt, p, /*tiles=*/true, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

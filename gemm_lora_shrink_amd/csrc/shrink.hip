@@ -1,0 +1,412 @@
+// Shrink: v[i][t][k] = scale[s] * sum_d A_i[s][k][d] * x[t][d] for every slice i
+// ("Add multi-LoRA support", the shrink of the punica kernels; the scale is
+// applied to the fp32 value), with the intermediate cleared inside the call
+// ("[LoRA] LoRA cuda graph specialization", Implementation).
+//
+// One launch covers the whole segment record.  Its work units are
+//   - the record's items, once per slice: a gather group (at most 16 tokens of
+//     one slot) or a segmented tile (at most 64 tokens of one slot).  For the
+//     item's tokens the unit computes D[token][rank] = X A_s^T, a [cnt x D] by
+//     [D x r_s] contraction, on the matrix cores with fp32 accumulation;
+//   - zero units: 64 consecutive entries of the record's tail of tokens without
+//     an adapter, whose v rows are cleared.
+// Every v row of the batch is written exactly once with plain stores: the rows
+// of active tokens with their values (0 in rank columns k >= r_s), the others
+// with zeros.  There is no separate clearing pass and no atomic, and the result
+// does not depend on how the units are scheduled.
+//
+// Inside a unit the four waves split the contraction index d between them.  A
+// K step is 16 bytes of every operand row per lane: 32 elements of a 16-bit
+// type (one v_mfma_f32_16x16x32) or 16 fp32 elements (four
+// v_mfma_f32_16x16x4f32).  Lane l supplies row l % 16 of a 16-row block and the
+// 16 bytes at element offset (l / 16) * 16 / sizeof(elem) of the step, for both
+// operands, so the contraction runs over exactly the d of the step.  Wave w takes
+// steps (round * 4 + w) * SB .. + SB - 1 of batch round `round`, so per round
+// the workgroup reads 4 * SB * 64 contiguous bytes of every row.  No operand is
+// shared between waves, so nothing is staged in LDS: each lane loads its MFMA
+// operands straight from global memory, and the next batch's loads are in
+// flight while the current batch is multiplied.  At the end the four waves'
+// partial sums meet in LDS, where each 16 x 16 block is summed, scaled and
+// stored by one wave.
+#include "common.h"
+
+namespace lora {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kZeroRows = 64;                                    // tail entries per zero unit
+constexpr int kMaxBlocks = (kTile / 16) * (LORA_MAX_RANK / 16);  // 16 accumulator blocks
+
+// One K step: one 16-byte operand per lane and 16-row block.
+template <typename Elem> struct StepMma;
+template <> struct StepMma<bf16_t> {
+  __device__ static inline f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+};
+template <> struct StepMma<half_t> {
+  __device__ static inline f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+};
+template <> struct StepMma<float> {
+  // Element e of every lane's 4 values forms one 16x16x4 product whose K index
+  // is the lane's 16-lane group: the four products together cover the 16
+  // elements of the step.
+  __device__ static inline f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ae = a[e], be = b[e];
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ae), __uint_as_float(be), c, 0, 0, 0);
+    }
+    return c;
+  }
+};
+
+// Steps per batch for RB token blocks and NB rank blocks (two batches are in
+// registers at a time, next to the RB x NB accumulator blocks).  Powers of two,
+// so that the common widths (D a multiple of 1024) split into whole pairs of
+// rounds.
+template <int RB, int NB> struct Batch {
+  static constexpr int kSteps = RB == 1 ? (NB == 1 ? 8 : 4) : (NB == 1 ? 4 : NB == 4 ? 1 : 2);
+};
+
+// Clear v columns [c0, r_max) of the unit's token rows (s_tok, -1 = none),
+// spread over the threads [first, first + count).
+__device__ inline void clear_columns(float* vb, int r_max, const int* s_tok, int cnt, int c0, int first, int count) {
+  const int w4 = (r_max - c0) / 4;  // r_max and c0 are multiples of 4
+  if (w4 <= 0) return;
+  for (int e = threadIdx.x - first; e < cnt * w4; e += count) {
+    const int row = e / w4, c = e - row * w4;
+    const int t = s_tok[row];
+    if (t >= 0) *reinterpret_cast<f32x4*>(vb + (int64_t)t * r_max + c0 + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// One (item, part, slice) unit with RB blocks of 16 tokens and NB blocks of 16
+// ranks, over the K steps [s0, s1) of the contraction.  s_tok holds the item's
+// tokens, -1 past the count (written before a barrier).  With `partial` the
+// unit is one of several parts of the contraction: it adds its sums to v with
+// atomics (v was cleared beforehand) and leaves the other columns alone;
+// otherwise it stores whole rows.
+template <typename Elem, int RB, int NB>
+__device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, int s, int r, int slice, int s0,
+                                              int s1, bool partial, f32x4 (*s_red)[kMaxBlocks][64],
+                                              const int* s_tok) {
+  using M = StepMma<Elem>;
+  constexpr int kVec = Traits<Elem>::kVec;
+  constexpr int kStep = 4 * kVec;  // elements per K step
+  constexpr int SB = Batch<RB, NB>::kSteps;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, m = lane & 15, kg = lane >> 4;
+
+  // Operand rows of this lane: token rb * 16 + m of the item and rank row
+  // nb * 16 + m.  Rows of a MFMA product do not mix, so a lane whose token or
+  // rank does not exist reads a row that does (the item's first token, the
+  // slot's last rank row): its outputs are discarded, and its loads hit the
+  // same addresses as another lane's.
+  // Addresses are a wave-uniform base plus a 32-bit byte offset per lane (the
+  // host checks that x and one slot's A rows each span less than 4 GiB).
+  const char* xb = reinterpret_cast<const char*>(p.x);
+  uint32_t xo[RB];
+  const int t0 = s_tok[0];  // cnt >= 1: a valid token
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int t = s_tok[rb * 16 + m];
+    xo[rb] = (uint32_t)(((int64_t)(t >= 0 ? t : t0) * p.ldx + kg * kVec) * (int64_t)sizeof(Elem));
+  }
+  const char* ab = reinterpret_cast<const char*>(p.A[slice]) + (int64_t)s * p.r_max * p.D * (int64_t)sizeof(Elem);
+  uint32_t ao[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int k = nb * 16 + m;
+    ao[nb] = (uint32_t)(((int64_t)(k < r ? k : r - 1) * p.D + kg * kVec) * (int64_t)sizeof(Elem));
+  }
+  auto at = [](const char* base, uint32_t off) { return *reinterpret_cast<const u32x4*>(base + off); };
+
+  f32x4 acc[RB][NB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Whole rounds: every load in range, addresses = row pointer + immediate.
+  auto load = [&](int round, u32x4 (&xd)[SB][RB], u32x4 (&ad)[SB][NB]) {
+    const uint32_t d0 = (uint32_t)(s0 + (round * kWaves + wave) * SB) * (uint32_t)(kStep * sizeof(Elem));
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const uint32_t di = d0 + i * kStep * (int)sizeof(Elem);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) xd[i][rb] = at(xb, xo[rb] + di);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) ad[i][nb] = at(ab, ao[nb] + di);
+    }
+  };
+  auto mul = [&](const u32x4 (&xd)[SB][RB], const u32x4 (&ad)[SB][NB]) {
+#pragma unroll
+    for (int i = 0; i < SB; ++i)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = M::mma(xd[i][rb], ad[i][nb], acc[rb][nb]);
+  };
+  // One step with the ragged end of D masked (D is a multiple of kVec, so each
+  // lane's 16 bytes are wholly inside or wholly outside).
+  auto load_step = [&](int j, u32x4 (&xd)[RB], u32x4 (&ad)[NB]) {
+    const int d = j * kStep;
+    const bool ok = j < s1 && d + kg * kVec < p.D;
+    const uint32_t db = ok ? (uint32_t)(d * (int)sizeof(Elem)) : 0u;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) xd[rb] = ld16_or0(xb + (xo[rb] + db), ok);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) ad[nb] = ld16_or0(ab + (ao[nb] + db), ok);
+  };
+  auto mul_step = [&](const u32x4 (&xd)[RB], const u32x4 (&ad)[NB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = M::mma(xd[rb], ad[nb], acc[rb][nb]);
+  };
+
+  // Pairs of whole rounds, software-pipelined: the next batch's loads are
+  // issued before the current batch is multiplied.
+  const int full_end = min(s1, p.D / kStep);  // steps before this lie wholly inside D
+  const int pairs = max(0, full_end - s0) / (2 * kWaves * SB);
+  // The scheduling barriers keep the compiler from sinking a batch's loads
+  // into the multiplications of the batch before (which would wait on them).
+  if (pairs > 0) {
+    u32x4 x0[SB][RB], a0[SB][NB], x1[SB][RB], a1[SB][NB];
+    load(0, x0, a0);
+    for (int pr = 0; pr + 1 < pairs; ++pr) {
+      load(2 * pr + 1, x1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(x0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(2 * pr + 2, x0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(x1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load(2 * pairs - 1, x1, a1);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(x0, a0);
+    mul(x1, a1);
+  }
+  // The steps left over (fewer than two rounds, the last possibly partial),
+  // two per wave at a time.
+  for (int j = s0 + pairs * 2 * kWaves * SB + wave; j < s1; j += 2 * kWaves) {
+    u32x4 xa[RB], aa[NB], xb[RB], ab2[NB];
+    load_step(j, xa, aa);
+    load_step(j + kWaves, xb, ab2);
+    mul_step(xa, aa);
+    mul_step(xb, ab2);
+  }
+
+  // Cross-wave sum through LDS: every wave leaves its blocks there (16 bytes
+  // per lane, conflict-free); block b is then summed, scaled and stored by wave
+  // b % 4, and the rank columns past the computed blocks are cleared.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s_red[wave][rb * NB + nb][lane] = acc[rb][nb];
+  __syncthreads();
+  float* vb = p.v + (int64_t)slice * p.v_slice_stride;
+  const float sc = p.scale ? p.scale[s] : 1.0f;
+#pragma unroll
+  for (int b = 0; b < RB * NB; ++b) {
+    if (b % kWaves != wave) continue;
+    const int rb = b / NB, nb = b % NB;
+    f32x4 a = s_red[0][b][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const f32x4 o = s_red[w][b][lane];
+      a[0] += o[0];
+      a[1] += o[1];
+      a[2] += o[2];
+      a[3] += o[3];
+    }
+    // lane (m, kg) holds D[token rb*16 + 4 kg + i][rank nb*16 + m]
+    const int k = nb * 16 + m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = s_tok[rb * 16 + 4 * kg + i];
+      if (partial) {
+        if (t >= 0 && k < r) atomicAdd(vb + (int64_t)t * p.r_max + k, a[i] * sc);
+      } else if (t >= 0 && k < p.r_max) {
+        vb[(int64_t)t * p.r_max + k] = k < r ? a[i] * sc : 0.f;
+      }
+    }
+  }
+  if (!partial) clear_columns(vb, p.r_max, s_tok, cnt, NB * 16, 0, kThreads);
+}
+
+// parts_t / parts_g: the contraction of every tile / group is cut into that
+// many parts (units of their own; more than 1 part means partial sums added
+// with atomics into a v cleared beforehand).  zero_units: clear the rows of
+// tokens without an adapter (not needed when v was cleared).
+template <typename Elem>
+__global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int parts_t, int parts_g,
+                                                            int zero_units) {
+  __shared__ f32x4 s_red[kWaves][kMaxBlocks][64];
+  __shared__ int s_tok[kTile];
+
+  const int32_t* rec = p.rec;
+  const bool rec_ok = rec[kBuiltT] == p.T && rec[kBuiltS] == p.S;
+  int na = rec_ok ? rec[kNumActive] : 0;
+  na = na < 0 ? 0 : (na > p.T ? p.T : na);
+  const int64_t n_t = parts_t > 0 ? (int64_t)record_items(rec, p.T, p.S, true) * parts_t : 0;
+  const int64_t n_g = parts_g > 0 ? (int64_t)record_items(rec, p.T, p.S, false) * parts_g : 0;
+  const int64_t n_z = zero_units ? (p.T - na + kZeroRows - 1) / kZeroRows : 0;
+  const int32_t* perm = rec + seg_layout(p.T, p.S).perm;
+
+  // Each of the three lists (tile parts, group parts, zero units; each unit
+  // once per slice, slice fastest so that the slices of one item share its x
+  // rows in one L2) is cut into 8 contiguous shares, one per XCD; the
+  // workgroups of an XCD walk the concatenation of its three shares.
+  const int64_t ns = p.n_slices;
+  const int64_t xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds, wgs = gridDim.x / kXcds;
+  auto share = [&](int64_t n, int64_t& st, int64_t& ln) {
+    const int64_t per = n / kXcds, rem = n % kXcds;
+    st = xcd * per + (xcd < rem ? xcd : rem);
+    ln = per + (xcd < rem ? 1 : 0);
+  };
+  int64_t st_t, ln_t, st_g, ln_g, st_z, ln_z;
+  share(n_t * ns, st_t, ln_t);
+  share(n_g * ns, st_g, ln_g);
+  share(n_z * ns, st_z, ln_z);
+  const int tid = threadIdx.x;
+
+  for (int64_t w = lb; w < ln_t + ln_g + ln_z; w += wgs) {
+    const int list = w < ln_t ? 0 : (w < ln_t + ln_g ? 1 : 2);
+    const int64_t unit = list == 0 ? st_t + w : (list == 1 ? st_g + (w - ln_t) : st_z + (w - ln_t - ln_g));
+    const int64_t ip = unit / ns;  // item * parts + part (zero units: chunk)
+    const int slice = (int)(unit - ip * ns);
+    float* vb = p.v + (int64_t)slice * p.v_slice_stride;
+
+    if (list == 2) {
+      // zero unit: tail entries na + 64 item .. of perm
+      const int w4 = p.r_max / 4;
+      const int64_t pos0 = na + ip * kZeroRows;
+      for (int e = tid; e < kZeroRows * w4; e += kThreads) {
+        const int row = e / w4, c = e - row * w4;
+        const int64_t pos = pos0 + row;
+        if (pos < p.T) {
+          const int t = rec_ok ? perm[pos] : (int)pos;
+          if (t >= 0 && t < p.T)
+            *reinterpret_cast<f32x4*>(vb + (int64_t)t * p.r_max + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      continue;  // no shared memory used: no barrier needed
+    }
+
+    // the item's header and its tokens arrive in one memory round trip
+    const bool tiles = list == 0;
+    const int parts = tiles ? parts_t : parts_g;
+    const int64_t item = ip / parts;
+    const int part = (int)(ip - item * parts);
+    const int cap = tiles ? kTile : kGroup;
+    const int32_t* it = item_ptr(rec, p.T, p.S, tiles, item);
+    const int tv = tid < cap ? it[4 + tid] : -1;
+    Item hd;
+    const bool ok = read_item(rec, p.T, p.S, tiles, item, hd);
+    if (!ok) continue;  // uniform
+    if (tid < kTile) s_tok[tid] = (tid < hd.cnt && tv >= 0 && tv < p.T) ? tv : -1;
+    __syncthreads();
+    const int s = __builtin_amdgcn_readfirstlane(hd.slot);
+    const int r = __builtin_amdgcn_readfirstlane(slot_rank(p.ranks, s, p.r_max));
+    const int nb = (r + 15) / 16;
+    // this part's K steps: parts take equal runs of whole steps
+    const int step_elems = 4 * Traits<Elem>::kVec;
+    const int n_steps = (p.D + step_elems - 1) / step_elems;
+    const int per_part = (n_steps + parts - 1) / parts;
+    const int s0 = min(n_steps, part * per_part), s1 = min(n_steps, s0 + per_part);
+    const bool partial = parts > 1;
+    if (nb == 0) {
+      if (!partial) clear_columns(vb, p.r_max, s_tok, hd.cnt, 0, 0, kThreads);
+    } else if (hd.cnt <= 16) {
+      switch (nb) {
+        case 1: contract_unit<Elem, 1, 1>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+        case 2: contract_unit<Elem, 1, 2>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+        case 3: contract_unit<Elem, 1, 3>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+        default: contract_unit<Elem, 1, 4>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+      }
+    } else {
+      switch (nb) {
+        case 1: contract_unit<Elem, 4, 1>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+        case 2: contract_unit<Elem, 4, 2>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+        case 3: contract_unit<Elem, 4, 3>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+        default: contract_unit<Elem, 4, 4>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+      }
+    }
+    __syncthreads();  // the next unit rewrites s_tok and s_red
+  }
+}
+
+// Parts per item so that the units of a list number about `target`: at least
+// 1, and no more than leaves each wave two K steps per part.
+int parts_for(int64_t cap_units, int n_steps, int64_t target) {
+  if (cap_units <= 0) return 1;
+  int64_t parts = (target + cap_units - 1) / cap_units;
+  const int64_t most = n_steps / (2 * kWaves);
+  if (parts > most) parts = most;
+  return parts < 1 ? 1 : (int)parts;
+}
+
+template <typename Elem>
+hipError_t launch(const ShrinkParams& p, bool groups, bool tiles, hipStream_t stream) {
+  const SegLayout L = seg_layout(p.T, p.S);
+  const void* kernel = reinterpret_cast<const void*>(&shrink_kernel<Elem>);
+  // The kernel is persistent.  A list whose items are too few to occupy the
+  // chip is cut into parts until its units number about three quarters of the
+  // workgroups the chip holds at once.
+  const int resident = persistent_grid(kernel, kThreads, 0, INT64_MAX / 4);
+  const int n_steps = (int)ceil_div(p.D, 4 * Traits<Elem>::kVec);
+  const int64_t target = resident * 3 / 4;
+  const int parts_t = tiles ? parts_for(L.cap_tiles * p.n_slices, n_steps, target) : 0;
+  const int parts_g = groups ? parts_for(L.cap_groups * p.n_slices, n_steps, target) : 0;
+  const bool cleared = parts_t > 1 || parts_g > 1;
+  if (cleared) {
+    // partial sums are added into v: clear it first (this also clears the
+    // rows of tokens without an adapter)
+    hipError_t e = launch_fill_zero(p.v, (int64_t)p.n_slices * p.v_slice_stride, stream);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t useful = ((tiles ? L.cap_tiles * parts_t : 0) + (groups ? L.cap_groups * parts_g : 0) +
+                          (cleared ? 0 : ceil_div(p.T, kZeroRows))) * p.n_slices;
+  const int grid = persistent_grid(kernel, kThreads, 0, useful);
+  hipLaunchKernelGGL(shrink_kernel<Elem>, dim3(grid), dim3(kThreads), 0, stream, p, parts_t, parts_g,
+                     cleared ? 0 : 1);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ v, int64_t n) {
+  const int64_t n4 = n >> 2;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    reinterpret_cast<f32x4*>(v)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) v[i] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(float* v, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = ceil_div(ceil_div(n, 4), 256);
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_shrink(lora_dtype dt, const ShrinkParams& p, bool groups, bool tiles, hipStream_t stream) {
+  switch (dt) {
+    case LORA_F32: return launch<float>(p, groups, tiles, stream);
+    case LORA_F16: return launch<half_t>(p, groups, tiles, stream);
+    case LORA_BF16: return launch<bf16_t>(p, groups, tiles, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lora

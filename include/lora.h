@@ -101,7 +101,9 @@ typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora
  *       info[8..15]           zero
  *   perm       [T]      at lora_segments_offset(T, S, LORA_SEG_PERM); the first
  *                       num_active entries are the active tokens ordered by slot
- *                       ascending, then token index ascending (stable)
+ *                       ascending, then token index ascending (stable); the
+ *                       remaining T - num_active entries are the other tokens
+ *                       (idx -1 or out of range), ascending
  *   seg_slot   [S]      at ..._SEG_SLOT; first num_segments entries: the
  *                       non-empty slots, ascending
  *   seg_start  [S + 1]  at ..._SEG_START; segment g is
@@ -178,6 +180,8 @@ lora_status lora_build_segments(const int32_t *idx, int32_t T, int32_t S, int32_
  *   scale    [S] fp32 device, nullable (= 1.0)
  *   v        [n_slices][T][r_max] fp32 device, written in full when the call
  *            runs: rows of inactive tokens and columns k >= r_s are 0
+ * x ((T - 1) * ldx + D elements) and one slot's A rows (r_max * D elements)
+ * must each span less than 4 GiB; otherwise LORA_ERR_UNSUPPORTED.
  */
 lora_status lora_shrink(lora_dtype dt, const void *x, int64_t ldx, int32_t T, int32_t D,
                         int32_t n_slices, const void *const *A, int32_t S, int32_t r_max,

@@ -80,6 +80,11 @@ def oracle_segments(idx, S):
                   ascending;
       seg_start   int32 [num_segments + 1]: segment g is perm[seg_start[g] :
                   seg_start[g+1]]; seg_start[-1] == num_active;
+      rest        int32 [T - num_active]: the tokens without a valid slot
+                  (idx -1 or out of range), ascending.  The pages do not
+                  describe this list; it is this library's reading of where
+                  the base-only tokens go in a record (after the active ones),
+                  so that the shrink can clear their intermediate rows;
       num_active, num_segments, max_seg_len, status.
     """
     idx = [int(v) for v in np.asarray(idx).reshape(-1)]
@@ -100,8 +105,10 @@ def oracle_segments(idx, S):
     seg_start = [0]
     for s in seg_slot:
         seg_start.append(seg_start[-1] + counts[s])
+    rest = [t for t in range(T) if not _valid_slot(idx[t], S)]
     return dict(
         perm=np.asarray(perm, dtype=np.int32),
+        rest=np.asarray(rest, dtype=np.int32),
         seg_slot=np.asarray(seg_slot, dtype=np.int32),
         seg_start=np.asarray(seg_start, dtype=np.int32),
         num_active=len(active),

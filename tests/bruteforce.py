@@ -67,7 +67,8 @@ def brute_segments(idx, S):
     counts = np.bincount(idx[act], minlength=S) if S > 0 else np.zeros(0, int)
     seg_slot = np.nonzero(counts)[0].astype(np.int32)
     seg_start = np.concatenate([[0], np.cumsum(counts[seg_slot])]).astype(np.int32)
-    return dict(perm=perm, seg_slot=seg_slot, seg_start=seg_start,
+    rest = np.nonzero(~valid)[0].astype(np.int32)
+    return dict(perm=perm, rest=rest, seg_slot=seg_slot, seg_start=seg_start,
                 num_active=int(act.size), num_segments=int(seg_slot.size),
                 max_seg_len=int(counts.max()) if counts.size else 0,
                 status=3 if bad else 0)

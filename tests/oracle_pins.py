@@ -331,7 +331,7 @@ def pin_handworked(o):
     assert np.array_equal(v[0], np.array(g["v"]).reshape(T, r)), "hand-worked v"
     assert np.array_equal(y, np.array(g["y"]).reshape(T, out)), "hand-worked y"
     seg = o.oracle_segments(idx, S)
-    for k in ("perm", "seg_slot", "seg_start"):
+    for k in ("perm", "rest", "seg_slot", "seg_start"):
         assert list(seg[k]) == [int(t) for t in g[k]], f"hand-worked {k}"
     for k in ("num_active", "num_segments", "max_seg_len", "status"):
         assert seg[k] == int(g[k][0]), f"hand-worked {k}"
@@ -374,7 +374,7 @@ def pin_segments(o):
     for n, (idx, S) in enumerate(segment_cases()):
         a = o.oracle_segments(idx, S)
         b = brute_segments(idx, S)
-        for k in ("perm", "seg_slot", "seg_start"):
+        for k in ("perm", "rest", "seg_slot", "seg_start"):
             assert np.array_equal(np.asarray(a[k]), b[k]) and a[k].dtype == np.int32, \
                 f"segments case {n}: {k}"
         for k in ("num_active", "num_segments", "max_seg_len", "status"):
@@ -382,6 +382,9 @@ def pin_segments(o):
         # invariants
         perm = a["perm"]
         assert sorted(perm.tolist()) == [t for t in range(len(idx)) if 0 <= idx[t] < S]
+        # perm followed by rest is a permutation of all tokens
+        assert sorted(perm.tolist() + a["rest"].tolist()) == list(range(len(idx)))
+        assert np.all(np.diff(a["rest"]) > 0)
         sl = idx[perm]
         assert np.all(np.diff(sl) >= 0)
         for g in range(a["num_segments"]):

@@ -35,6 +35,7 @@ def check_record(idx, S, mode, label):
     assert info[2] == ref["max_seg_len"] and info[3] == ref["status"], label
     assert info[6] == T and info[7] == S and not np.any(info[8:]), label
     assert np.array_equal(rec[off["perm"]:off["perm"] + na], ref["perm"]), label
+    assert np.array_equal(rec[off["perm"] + na:off["perm"] + T], ref["rest"]), label
     assert np.array_equal(rec[off["seg_slot"]:off["seg_slot"] + ns], ref["seg_slot"]), label
     assert np.array_equal(rec[off["seg_start"]:off["seg_start"] + ns + 1], ref["seg_start"]), label
 
@@ -98,7 +99,7 @@ def specified_words(rec, T, S):
     off = {k: glsa.segments_offset(T, S, k) for k in glsa.SEG_FIELDS}
     info = rec[:16]
     return np.concatenate([
-        info, rec[off["perm"]:off["perm"] + info[0]],
+        info, rec[off["perm"]:off["perm"] + T],
         rec[off["seg_slot"]:off["seg_slot"] + info[1]],
         rec[off["seg_start"]:off["seg_start"] + info[1] + 1],
         rec[off["groups"]:off["groups"] + 20 * info[4]],
