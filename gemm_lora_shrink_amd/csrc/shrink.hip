@@ -16,18 +16,21 @@
 // does not depend on how the units are scheduled.
 //
 // Inside a unit the four waves split the contraction index d between them.  A
-// K step is 16 bytes of every operand row per lane: 32 elements of a 16-bit
-// type (one v_mfma_f32_16x16x32) or 16 fp32 elements (four
-// v_mfma_f32_16x16x4f32).  Lane l supplies row l % 16 of a 16-row block and the
-// 16 bytes at element offset (l / 16) * 16 / sizeof(elem) of the step, for both
-// operands, so the contraction runs over exactly the d of the step.  Wave w takes
-// steps (round * 4 + w) * SB .. + SB - 1 of batch round `round`, so per round
-// the workgroup reads 4 * SB * 64 contiguous bytes of every row.  No operand is
-// shared between waves, so nothing is staged in LDS: each lane loads its MFMA
-// operands straight from global memory, and the next batch's loads are in
-// flight while the current batch is multiplied.  At the end the four waves'
-// partial sums meet in LDS, where each 16 x 16 block is summed, scaled and
-// stored by one wave.
+// K step is 64 bytes of every operand row: 32 elements of a 16-bit type (one
+// v_mfma_f32_16x16x32) or 16 fp32 elements (four v_mfma_f32_16x16x4f32).  A
+// batch is two steps, one 128-byte cache line of every row; wave w takes batches
+// w, w + 4, w + 8, .. so that the workgroup reads 512 contiguous bytes of each
+// row per round.  MFMA wants lane l to hold 16 bytes of row l % 16, so loading
+// operands straight into registers makes every group of 16 lanes touch 16
+// different rows, and a compute unit then streams only about a third of what it
+// does with whole-line accesses.  Each wave therefore copies its batches into
+// its own LDS ring with global-to-LDS loads in which 8 lanes fetch one whole
+// row line, several batches ahead, and reads them back in MFMA layout.  The 16
+// byte pieces of a row are stored XOR-swizzled by row so that those reads are
+// free of bank conflicts.  Only the wave's own loads fill its ring, so the
+// wave waits on its own load counter and no barrier is needed.  At the end the
+// four waves' partial sums meet in LDS, where each 16 x 16 block is summed,
+// scaled and stored by one wave.
 #include "common.h"
 
 namespace lora {
@@ -37,7 +40,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kZeroRows = 64;                                    // tail entries per zero unit
-constexpr int kMaxBlocks = (kTile / 16) * (LORA_MAX_RANK / 16);  // 16 accumulator blocks
 
 // One K step: one 16-byte operand per lane and 16-row block.
 template <typename Elem> struct StepMma;
@@ -67,13 +69,47 @@ template <> struct StepMma<float> {
   }
 };
 
-// Steps per batch for RB token blocks and NB rank blocks (two batches are in
-// registers at a time, next to the RB x NB accumulator blocks).  Powers of two,
-// so that the common widths (D a multiple of 1024) split into whole pairs of
-// rounds.
-template <int RB, int NB> struct Batch {
-  static constexpr int kSteps = RB == 1 ? (NB == 1 ? 8 : 4) : (NB == 1 ? 4 : NB == 4 ? 1 : 2);
-};
+constexpr int kRingBytes = 32768;  // LDS ring of one wave (also holds its partial sums)
+constexpr int kBlockBytes = 2048;  // one batch of one 16-row block: 16 rows x 128 bytes
+
+// One global-to-LDS load: every lane fetches the 16 bytes at base + voff (base
+// wave-uniform) and they land at LDS byte lds + 16 * lane.  Issued by hand: the
+// compiler, which cannot tell the ring's slots apart, would otherwise wait for
+// every load in flight before each LDS read.  M0 is saved and restored around
+// it.
+__device__ inline void load_to_lds(const char* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory");
+}
+
+// Wait until at most n (a multiple of `unit`, at most 7 units and at most 63,
+// the counter's range) of this wave's vector memory operations are outstanding.
+template <int k, int unit>
+__device__ inline void wait_vm_const() {
+  constexpr int n = k * unit < 63 ? k * unit : 63;  // larger cases never occur
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
+template <int unit>
+__device__ inline void wait_vm(int n) {
+  switch (n / unit) {
+    case 0: wait_vm_const<0, unit>(); break;
+    case 1: wait_vm_const<1, unit>(); break;
+    case 2: wait_vm_const<2, unit>(); break;
+    case 3: wait_vm_const<3, unit>(); break;
+    case 4: wait_vm_const<4, unit>(); break;
+    case 5: wait_vm_const<5, unit>(); break;
+    case 6: wait_vm_const<6, unit>(); break;
+    default: wait_vm_const<7, unit>(); break;
+  }
+}
 
 // Clear v columns [c0, r_max) of the unit's token rows (s_tok, -1 = none),
 // spread over the threads [first, first + count).
@@ -89,43 +125,60 @@ __device__ inline void clear_columns(float* vb, int r_max, const int* s_tok, int
 
 // One (item, part, slice) unit with RB blocks of 16 tokens and NB blocks of 16
 // ranks, over the K steps [s0, s1) of the contraction.  s_tok holds the item's
-// tokens, -1 past the count (written before a barrier).  With `partial` the
-// unit is one of several parts of the contraction: it adds its sums to v with
-// atomics (v was cleared beforehand) and leaves the other columns alone;
-// otherwise it stores whole rows.
+// tokens, -1 past the count (written before a barrier); s_lds is the
+// workgroup's four rings.  With `partial` the unit is one of several parts of
+// the contraction: it adds its sums to v with atomics (v was cleared
+// beforehand) and leaves the other columns alone; otherwise it stores whole
+// rows.
 template <typename Elem, int RB, int NB>
 __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, int s, int r, int slice, int s0,
-                                              int s1, bool partial, f32x4 (*s_red)[kMaxBlocks][64],
-                                              const int* s_tok) {
+                                              int s1, bool partial, char* s_lds, const int* s_tok) {
   using M = StepMma<Elem>;
   constexpr int kVec = Traits<Elem>::kVec;
-  constexpr int kStep = 4 * kVec;  // elements per K step
-  constexpr int SB = Batch<RB, NB>::kSteps;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, m = lane & 15, kg = lane >> 4;
+  constexpr int kStep = 4 * kVec;  // elements per K step (64 bytes)
+  constexpr int NBLK = RB + NB;
+  constexpr int kSlot = NBLK * kBlockBytes;              // one batch of every block
+  constexpr int DEPTH = kRingBytes / kSlot < 8 ? kRingBytes / kSlot : 8;
+  constexpr int IPB = 2 * NBLK;                          // loads per batch
+  static_assert((DEPTH - 1) * IPB <= 63, "the ring's loads must fit the wait counter");
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, kg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  char* ring = s_lds + wave * kRingBytes;
 
-  // Operand rows of this lane: token rb * 16 + m of the item and rank row
-  // nb * 16 + m.  Rows of a MFMA product do not mix, so a lane whose token or
-  // rank does not exist reads a row that does (the item's first token, the
-  // slot's last rank row): its outputs are discarded, and its loads hit the
-  // same addresses as another lane's.
-  // Addresses are a wave-uniform base plus a 32-bit byte offset per lane (the
-  // host checks that x and one slot's A rows each span less than 4 GiB).
+  // Operand rows.  Block bk < RB holds tokens bk * 16 .. of the item, block
+  // RB + nb rank rows nb * 16 ..  Rows of a MFMA product do not mix, so a row
+  // whose token or rank does not exist is read from one that does (the item's
+  // first token, the slot's last rank row): its outputs are discarded, and its
+  // loads hit addresses another lane loads too.  Addresses are a wave-uniform
+  // base plus a 32-bit byte offset (the host checks that x and one slot's A rows
+  // each span less than 4 GiB).
+  //
+  // Global-to-LDS load q (0, 1) of a block: lane l fetches row 8 q + l / 8, the
+  // 16-byte piece (l % 8) ^ (l / 8) of the batch's line of that row, and lands
+  // at byte 16 l of the load's 1 KB.
   const char* xb = reinterpret_cast<const char*>(p.x);
-  uint32_t xo[RB];
-  const int t0 = s_tok[0];  // cnt >= 1: a valid token
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int t = s_tok[rb * 16 + m];
-    xo[rb] = (uint32_t)(((int64_t)(t >= 0 ? t : t0) * p.ldx + kg * kVec) * (int64_t)sizeof(Elem));
-  }
   const char* ab = reinterpret_cast<const char*>(p.A[slice]) + (int64_t)s * p.r_max * p.D * (int64_t)sizeof(Elem);
-  uint32_t ao[NB];
+  const int t0 = s_tok[0];  // cnt >= 1: a valid token
+  const uint32_t piece = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  uint32_t so[NBLK][2];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int k = nb * 16 + m;
-    ao[nb] = (uint32_t)(((int64_t)(k < r ? k : r - 1) * p.D + kg * kVec) * (int64_t)sizeof(Elem));
+  for (int q = 0; q < 2; ++q) {
+    const int row = 8 * q + (lane >> 3);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int t = s_tok[rb * 16 + row];
+      so[rb][q] = (uint32_t)((int64_t)(t >= 0 ? t : t0) * p.ldx * (int64_t)sizeof(Elem)) + piece;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int k = nb * 16 + row;
+      so[RB + nb][q] = (uint32_t)((int64_t)(k < r ? k : r - 1) * p.D * (int64_t)sizeof(Elem)) + piece;
+    }
   }
-  auto at = [](const char* base, uint32_t off) { return *reinterpret_cast<const u32x4*>(base + off); };
+  // MFMA reads: step j of a batch gives K slot kg the piece 4 j + kg of row m
+  uint32_t rd[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) rd[j] = (uint32_t)((m >> 3) * 1024 + (m & 7) * 128 + (((4 * j + kg) ^ (m & 7)) * 16));
 
   f32x4 acc[RB][NB];
 #pragma unroll
@@ -133,85 +186,82 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Whole rounds: every load in range, addresses = row pointer + immediate.
-  auto load = [&](int round, u32x4 (&xd)[SB][RB], u32x4 (&ad)[SB][NB]) {
-    const uint32_t d0 = (uint32_t)(s0 + (round * kWaves + wave) * SB) * (uint32_t)(kStep * sizeof(Elem));
+  // batches of this unit: b covers steps s0 + 2 b, s0 + 2 b + 1; the full ones
+  // lie wholly inside D and [s0, s1)
+  const int full_end = min(s1, p.D / kStep);
+  const int n_full = max(0, (full_end - s0) / 2);
+  const int my_n = n_full > wave ? (n_full - wave + kWaves - 1) / kWaves : 0;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;  // LDS byte address of the ring
+  auto issue = [&](int i) {  // the wave's i-th batch into ring slot i % DEPTH
+    const uint32_t boff = (uint32_t)(s0 + 2 * (wave + kWaves * i)) * 64u;
+    const uint32_t dst = ring_lds + (uint32_t)((i % DEPTH) * kSlot);
 #pragma unroll
-    for (int i = 0; i < SB; ++i) {
-      const uint32_t di = d0 + i * kStep * (int)sizeof(Elem);
+    for (int bk = 0; bk < NBLK; ++bk)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) xd[i][rb] = at(xb, xo[rb] + di);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) ad[i][nb] = at(ab, ao[nb] + di);
-    }
+      for (int q = 0; q < 2; ++q)
+        load_to_lds(bk < RB ? xb : ab, so[bk][q] + boff, dst + (uint32_t)(bk * kBlockBytes + q * 1024));
   };
-  auto mul = [&](const u32x4 (&xd)[SB][RB], const u32x4 (&ad)[SB][NB]) {
+  int issued = 0;
+  for (; issued < my_n && issued < DEPTH; ++issued) issue(issued);
+  for (int i = 0; i < my_n; ++i) {
+    wait_vm<IPB>((issued - i - 1) * IPB);  // batch i has landed
+    const char* slot = ring + (i % DEPTH) * kSlot;
 #pragma unroll
-    for (int i = 0; i < SB; ++i)
+    for (int j = 0; j < 2; ++j) {
+      u32x4 op[NBLK];
+#pragma unroll
+      for (int bk = 0; bk < NBLK; ++bk) op[bk] = *reinterpret_cast<const u32x4*>(slot + bk * kBlockBytes + rd[j]);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = M::mma(xd[i][rb], ad[i][nb], acc[rb][nb]);
-  };
-  // One step with the ragged end of D masked (D is a multiple of kVec, so each
-  // lane's 16 bytes are wholly inside or wholly outside).
-  auto load_step = [&](int j, u32x4 (&xd)[RB], u32x4 (&ad)[NB]) {
-    const int d = j * kStep;
-    const bool ok = j < s1 && d + kg * kVec < p.D;
-    const uint32_t db = ok ? (uint32_t)(d * (int)sizeof(Elem)) : 0u;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) xd[rb] = ld16_or0(xb + (xo[rb] + db), ok);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) ad[nb] = ld16_or0(ab + (ao[nb] + db), ok);
-  };
-  auto mul_step = [&](const u32x4 (&xd)[RB], const u32x4 (&ad)[NB]) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = M::mma(xd[rb], ad[nb], acc[rb][nb]);
-  };
-
-  // Pairs of whole rounds, software-pipelined: the next batch's loads are
-  // issued before the current batch is multiplied.
-  const int full_end = min(s1, p.D / kStep);  // steps before this lie wholly inside D
-  const int pairs = max(0, full_end - s0) / (2 * kWaves * SB);
-  // The scheduling barriers keep the compiler from sinking a batch's loads
-  // into the multiplications of the batch before (which would wait on them).
-  if (pairs > 0) {
-    u32x4 x0[SB][RB], a0[SB][NB], x1[SB][RB], a1[SB][NB];
-    load(0, x0, a0);
-    for (int pr = 0; pr + 1 < pairs; ++pr) {
-      load(2 * pr + 1, x1, a1);
-      __builtin_amdgcn_sched_barrier(0);
-      mul(x0, a0);
-      __builtin_amdgcn_sched_barrier(0);
-      load(2 * pr + 2, x0, a0);
-      __builtin_amdgcn_sched_barrier(0);
-      mul(x1, a1);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = M::mma(op[rb], op[RB + nb], acc[rb][nb]);
     }
-    load(2 * pairs - 1, x1, a1);
+    // the slot is refilled only after its reads are done
     __builtin_amdgcn_sched_barrier(0);
-    mul(x0, a0);
-    mul(x1, a1);
-  }
-  // The steps left over (fewer than two rounds, the last possibly partial),
-  // two per wave at a time.
-  for (int j = s0 + pairs * 2 * kWaves * SB + wave; j < s1; j += 2 * kWaves) {
-    u32x4 xa[RB], aa[NB], xb[RB], ab2[NB];
-    load_step(j, xa, aa);
-    load_step(j + kWaves, xb, ab2);
-    mul_step(xa, aa);
-    mul_step(xb, ab2);
+    if (issued < my_n) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(issued);
+      ++issued;
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Cross-wave sum through LDS: every wave leaves its blocks there (16 bytes
-  // per lane, conflict-free); block b is then summed, scaled and stored by wave
+  // the batch that reaches past the end of D or of the part (at most one):
+  // masked loads straight into registers
+  if (n_full * 2 < s1 - s0 && n_full % kWaves == wave) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int step = s0 + 2 * n_full + j;
+      const int d = step * kStep + kg * kVec;
+      const bool ok = step < s1 && d < p.D;
+      u32x4 op[NBLK];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int t = s_tok[rb * 16 + m];
+        const char* row = xb + (int64_t)(t >= 0 ? t : t0) * p.ldx * (int64_t)sizeof(Elem);
+        op[rb] = ld16_or0(row + (ok ? (int64_t)d * (int64_t)sizeof(Elem) : 0), ok);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int k = nb * 16 + m;
+        const char* row = ab + (int64_t)(k < r ? k : r - 1) * p.D * (int64_t)sizeof(Elem);
+        op[RB + nb] = ld16_or0(row + (ok ? (int64_t)d * (int64_t)sizeof(Elem) : 0), ok);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = M::mma(op[rb], op[RB + nb], acc[rb][nb]);
+    }
+  }
+
+  // Cross-wave sum: each wave leaves its blocks in its own ring (16 bytes per
+  // lane, conflict-free); block b is then summed, scaled and stored by wave
   // b % 4, and the rank columns past the computed blocks are cleared.
+  f32x4* red = reinterpret_cast<f32x4*>(ring);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s_red[wave][rb * NB + nb][lane] = acc[rb][nb];
+    for (int nb = 0; nb < NB; ++nb) red[(rb * NB + nb) * 64 + lane] = acc[rb][nb];
   __syncthreads();
   float* vb = p.v + (int64_t)slice * p.v_slice_stride;
   const float sc = p.scale ? p.scale[s] : 1.0f;
@@ -219,10 +269,10 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
   for (int b = 0; b < RB * NB; ++b) {
     if (b % kWaves != wave) continue;
     const int rb = b / NB, nb = b % NB;
-    f32x4 a = s_red[0][b][lane];
+    f32x4 a = reinterpret_cast<const f32x4*>(s_lds)[b * 64 + lane];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      const f32x4 o = s_red[w][b][lane];
+      const f32x4 o = reinterpret_cast<const f32x4*>(s_lds + w * kRingBytes)[b * 64 + lane];
       a[0] += o[0];
       a[1] += o[1];
       a[2] += o[2];
@@ -248,9 +298,9 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
 // with atomics into a v cleared beforehand).  zero_units: clear the rows of
 // tokens without an adapter (not needed when v was cleared).
 template <typename Elem>
-__global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int parts_t, int parts_g,
+__global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int parts_t, int parts_g,
                                                             int zero_units) {
-  __shared__ f32x4 s_red[kWaves][kMaxBlocks][64];
+  __shared__ __attribute__((aligned(1024))) char s_lds[kWaves * kRingBytes];
   __shared__ int s_tok[kTile];
 
   const int32_t* rec = p.rec;
@@ -328,20 +378,20 @@ __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int
       if (!partial) clear_columns(vb, p.r_max, s_tok, hd.cnt, 0, 0, kThreads);
     } else if (hd.cnt <= 16) {
       switch (nb) {
-        case 1: contract_unit<Elem, 1, 1>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
-        case 2: contract_unit<Elem, 1, 2>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
-        case 3: contract_unit<Elem, 1, 3>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
-        default: contract_unit<Elem, 1, 4>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+        case 1: contract_unit<Elem, 1, 1>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
+        case 2: contract_unit<Elem, 1, 2>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
+        case 3: contract_unit<Elem, 1, 3>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
+        default: contract_unit<Elem, 1, 4>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
       }
     } else {
       switch (nb) {
-        case 1: contract_unit<Elem, 4, 1>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
-        case 2: contract_unit<Elem, 4, 2>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
-        case 3: contract_unit<Elem, 4, 3>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
-        default: contract_unit<Elem, 4, 4>(p, hd.cnt, s, r, slice, s0, s1, partial, s_red, s_tok); break;
+        case 1: contract_unit<Elem, 4, 1>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
+        case 2: contract_unit<Elem, 4, 2>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
+        case 3: contract_unit<Elem, 4, 3>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
+        default: contract_unit<Elem, 4, 4>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
       }
     }
-    __syncthreads();  // the next unit rewrites s_tok and s_red
+    __syncthreads();  // the next unit rewrites s_tok and the rings
   }
 }
 
