@@ -4,22 +4,30 @@
 // compilation", review of the token index buffer); every LoRA layer of the
 // batch then reuses this record.
 //
-// One workgroup of 1024 threads (16 waves of 64) does everything, so the result
-// is bit-exact and deterministic:
-//   1. per-slot token counts (LDS atomics: counts do not depend on order);
-//   2. a block-wide exclusive scan over slots giving each slot's start in perm,
-//      its segment number and the offsets of its work items;
-//   3. the segment tables, the info words and the work items;
-//   4. a stable scatter of the tokens into perm, 1024 tokens per chunk: inside a
-//      wave, lanes holding the same slot find each other with ballots; across
-//      the 16 waves a per-(wave, slot) count table gives each wave its offset in
-//      wave order.  No atomics touch the order.  Tokens without a valid slot
-//      are placed as if they had slot S, after all active tokens, so perm ends
-//      with them in ascending order (the shrink clears their v rows);
-//   5. the work items, each followed by its token indices, read back from an
-//      LDS mirror of perm (from global memory past 8192 tokens).
-// The first 8192 slot indices are loaded once, all at the same time, and kept
-// in registers.
+// One workgroup of 1024 threads (16 waves) does everything, so the result is
+// bit-exact and deterministic.  Wave w owns the contiguous token range
+// [w R, (w + 1) R), walked in chunks of 64 (one token per lane).  The key of a
+// token is its slot, or S for a token without a valid slot (those follow every
+// active token in perm, ascending, and the shrink clears their v rows).
+//   1. Counts: in each chunk the lanes with one key find each other with one
+//      ballot per bit of the key; the lowest of them adds their number to the
+//      wave's row of a per-(wave, key) count table.  No atomics.
+//   2. One thread per key sums its column of the table, a block-wide scan over
+//      slots gives each slot's start in perm, its segment number and the
+//      offsets of its work items, and the column is turned into the start of
+//      each wave's run of that key.  Segment tables and info words follow.
+//   3. Scatter: each wave walks its range again; a token lands at its wave's
+//      run start for its key plus its rank among the chunk's lanes with that
+//      key, and the run start advances by their number.  Ranges, chunks and
+//      lanes are all in token order, so the placement is stable, and since a
+//      wave only touches its own row no barrier is needed.
+//   4. Work items, each followed by its token indices, read back from an LDS
+//      mirror of perm (from global memory past 8192 tokens).
+// Chunks held in registers keep their keys and lane masks from step 1 to step
+// 3.  Barriers that only order LDS traffic do not wait for the record's global
+// stores.
+#include <type_traits>
+
 #include "common.h"
 
 namespace lora {
@@ -28,8 +36,32 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kRegChunks = 8;   // chunks per wave kept in registers
+constexpr int kLdsPerm = 8192;  // perm positions mirrored in LDS
+constexpr int kItemTab = 2048;  // items whose slot is tabulated in LDS
 
 __device__ inline int lane_id() { return __lane_id(); }
+
+// Workgroup barrier for data exchanged through LDS only.  __syncthreads() also
+// orders global memory, so it waits for every outstanding global store (the
+// perm and table writes) first; here only this wave's LDS operations are
+// waited for.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Lanes of this wave (valid ones only) whose key equals this lane's: one ballot
+// per bit of the key, keys being below 2^nbits; a chunk whose valid lanes all
+// hold one key (a prefill segment) needs a single ballot.
+__device__ inline uint64_t wave_peers(int key, bool valid, int nbits) {
+  uint64_t peers = __ballot(valid);
+  const int first = __builtin_amdgcn_readlane(key, peers ? __builtin_ctzll(peers) : 0);
+  if (__ballot(valid && key == first) == peers) return valid ? peers : 0;  // uniform
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return valid ? peers : 0;
+}
 
 // Inclusive scan of one int across the wave.
 __device__ inline int wave_inclusive_scan(int v) {
@@ -43,17 +75,27 @@ __device__ inline int wave_inclusive_scan(int v) {
 }
 
 // Block-wide exclusive scan of four ints per thread (thread order), returning
-// the exclusive prefixes and writing the four totals to `total`.
-__device__ inline void block_exclusive_scan4(int4& v, int4* wave_sums, int4& total) {
+// the exclusive prefixes and writing the four totals to `total`.  Only threads
+// below S hold nonzero values; with S <= 64 one wave's scan is the whole scan.
+__device__ inline void block_exclusive_scan4(int4& v, int4* wave_sums, int4& total, int S) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  int4 inc;
-  inc.x = wave_inclusive_scan(v.x);
-  inc.y = wave_inclusive_scan(v.y);
-  inc.z = wave_inclusive_scan(v.z);
-  inc.w = wave_inclusive_scan(v.w);
+  int4 inc = v;  // waves past the slots hold zeros: their scan is the identity
+  if (wave * 64 < S) {  // uniform
+    inc.x = wave_inclusive_scan(v.x);
+    inc.y = wave_inclusive_scan(v.y);
+    inc.z = wave_inclusive_scan(v.z);
+    inc.w = wave_inclusive_scan(v.w);
+  }
+  if (S <= 64) {  // uniform
+    if (wave == 0 && lane == 63) wave_sums[0] = inc;
+    lds_barrier();
+    total = wave_sums[0];
+    v = make_int4(inc.x - v.x, inc.y - v.y, inc.z - v.z, inc.w - v.w);
+    return;
+  }
   if (lane == 63) wave_sums[wave] = inc;
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {
     int4 w = lane < kWaves ? wave_sums[lane] : make_int4(0, 0, 0, 0);
     int4 wi;
@@ -64,7 +106,7 @@ __device__ inline void block_exclusive_scan4(int4& v, int4* wave_sums, int4& tot
     if (lane < kWaves) wave_sums[lane] = make_int4(wi.x - w.x, wi.y - w.y, wi.z - w.z, wi.w - w.w);
     if (lane == kWaves - 1) wave_sums[kWaves] = wi;
   }
-  __syncthreads();
+  lds_barrier();
   int4 base = wave_sums[wave];
   total = wave_sums[kWaves];
   v = make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
@@ -80,153 +122,121 @@ __device__ inline int upper_slot(const int* arr, int n, int key) {
   return lo;
 }
 
-constexpr int kRegChunks = 8;                  // idx chunks held in registers (T <= 8192)
-constexpr int kLdsPerm = kRegChunks * kThreads;  // perm positions mirrored in LDS
-
-// Stable placement of one chunk of 1024 tokens (t = c0 + tid, slot index s).
-// A token whose s is not a valid slot takes key S: those tokens follow every
-// active token in perm.  Lanes with t >= T place nothing.
-__device__ inline void scatter_chunk(int t, int s, int T, int S, int32_t* __restrict__ perm, int* s_perm, int* s_run,
-                                     uint8_t (*s_wtab)[LORA_MAX_SLOTS + 1], int* s_leader_base) {
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = tid >> 6;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const bool valid = t < T;
-  s = (s >= 0 && s < S) ? s : S;
-  // lanes of this wave with the same key
-  uint64_t remaining = __ballot(valid);
-  uint64_t peers = 0;
-  while (remaining) {
-    const int leader = __builtin_ctzll(remaining);
-    const int ls = __shfl(s, leader, 64);
-    const uint64_t m = __ballot(valid && s == ls);
-    if (valid && s == ls) peers = m;
-    remaining &= ~m;
-  }
-  const bool is_leader = valid && (peers & lt_mask) == 0;
-  const int wcount = __popcll(peers);
-  if (is_leader) s_wtab[wave][s] = (uint8_t)wcount;
-  __syncthreads();
-  int base = 0;
-  bool last_wave = false;
-  if (is_leader) {
-    int pre = 0, post = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = s_wtab[w][s];
-      if (w < wave) pre += c;
-      if (w > wave) post += c;
-    }
-    base = s_run[s] + pre;
-    last_wave = (post == 0);
-    s_leader_base[tid] = base;
-  }
-  __syncthreads();
-  if (valid) {
-    const int pos = s_leader_base[(wave << 6) + __builtin_ctzll(peers)] + __popcll(peers & lt_mask);
-    perm[pos] = t;
-    if (pos < kLdsPerm) s_perm[pos] = t;
-  }
-  if (is_leader) {
-    s_wtab[wave][s] = 0;
-    if (last_wave) s_run[s] = base + wcount;
-  }
-  __syncthreads();
-}
-
 __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t* __restrict__ idx, int T, int S,
                                                                   int mode, int32_t* __restrict__ rec) {
+  __shared__ int s_tab[kWaves][LORA_MAX_SLOTS + 1];  // per-(wave, key) counts, then run starts
   __shared__ int s_count[LORA_MAX_SLOTS];
   __shared__ int s_start[LORA_MAX_SLOTS];
-  __shared__ int s_run[LORA_MAX_SLOTS + 1];  // [S]: the tokens without a slot
   __shared__ int s_seg[LORA_MAX_SLOTS];
   __shared__ int s_gofs[LORA_MAX_SLOTS + 1];
   __shared__ int s_tofs[LORA_MAX_SLOTS + 1];
-  __shared__ uint8_t s_wtab[kWaves][LORA_MAX_SLOTS + 1];
-  __shared__ int s_leader_base[kThreads];
+  __shared__ int16_t s_gslot[kItemTab];  // slot of gather item i
+  __shared__ int16_t s_tslot[kItemTab];  // slot of segmented item i
   __shared__ int s_perm[kLdsPerm];
   __shared__ int4 s_wave_sums[kWaves + 1];
   __shared__ int s_bad, s_maxlen;
 
   const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const SegLayout L = seg_layout(T, S);
   int32_t* perm = rec + L.perm;
+  const int R = (int)ceil_div(ceil_div(T, kWaves), 64) * 64;  // tokens per wave
+  const int n_chunks = R / 64;
+  const int t_begin = wave * R;
+  const int nbits = 32 - __builtin_clz((unsigned)S);  // keys 0 .. S
 
-  // the first 8192 slot indices stay in registers; all loads are issued at once
-  int my_idx[kRegChunks];
+  // the first kRegChunks chunks of the wave's slot indices are loaded at once
+  int key[kRegChunks];
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c) {
-    const int t = c * kThreads + tid;
-    const int32_t* src = t < T ? idx + t : reinterpret_cast<const int32_t*>(g_zero16);  // idx may be null when T = 0
-    my_idx[c] = *src;
-    if (t >= T) my_idx[c] = -1;
+    const int t = t_begin + c * 64 + lane;
+    const bool in = c < n_chunks && t < T;
+    const int32_t* src = in ? idx + t : reinterpret_cast<const int32_t*>(g_zero16);  // idx may be null when T = 0
+    key[c] = *src;
   }
 
-  for (int s = tid; s <= S; s += kThreads) {
-    if (s < S) s_count[s] = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s_wtab[w][s] = 0;
-  }
+  for (int e = tid; e < kWaves * (S + 1); e += kThreads) s_tab[e / (S + 1)][e % (S + 1)] = 0;
   if (tid == 0) {
     s_bad = 0;
     s_maxlen = 0;
   }
-  __syncthreads();
+  lds_barrier();
 
-  // 1. counts
+  // 1. per-(wave, key) counts
   int bad = 0;
+  uint64_t peers_reg[kRegChunks];
+  auto count_chunk = [&](int t, int& k) -> uint64_t {
+    const bool valid = t < T;
+    if (valid && !(k >= 0 && k < S)) {
+      if (k != -1) bad = 1;
+      k = S;
+    }
+    const uint64_t peers = wave_peers(k, valid, nbits);
+    if (valid && (peers & lt_mask) == 0) s_tab[wave][k] += __popcll(peers);  // one lane per key
+    return peers;
+  };
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c) {
-    const int s = my_idx[c];
-    if (s >= 0 && s < S) atomicAdd(&s_count[s], 1);
-    else if (s != -1) bad = 1;
+    peers_reg[c] = 0;
+    if (c < n_chunks) peers_reg[c] = count_chunk(t_begin + c * 64 + lane, key[c]);  // uniform condition
   }
-  for (int t = kRegChunks * kThreads + tid; t < T; t += kThreads) {
-    const int s = idx[t];
-    if (s >= 0 && s < S) atomicAdd(&s_count[s], 1);
-    else if (s != -1) bad = 1;
+  for (int c = kRegChunks; c < n_chunks; ++c) {
+    const int t = t_begin + c * 64 + lane;
+    int k = t < T ? idx[t] : -1;
+    count_chunk(t, k);
   }
   if (bad) s_bad = 1;  // benign: every writer stores 1
-  __syncthreads();
+  lds_barrier();
 
-  // 2. scans over slots; thread tid owns slot tid (S <= 1024 = kThreads)
-  const int n = tid < S ? s_count[tid] : 0;
-  int ng = 0, nt = 0;
-  if (n > 0) {
-    const bool to_tiles = (mode == LORA_MODE_SGMV) || (mode == LORA_MODE_AUTO && n >= kSgmvMinTokens);
-    if (to_tiles) nt = (int)ceil_div(n, kTile);
-    else ng = (int)ceil_div(n, kGroup);
-    atomicMax(&s_maxlen, n);
-  }
-  int4 sc = make_int4(n, n > 0 ? 1 : 0, ng, nt);
-  int4 tot;
-  block_exclusive_scan4(sc, s_wave_sums, tot);
+  // 2. scan over slots (thread tid owns slot tid; S <= 1024), then run starts
+  int n_slot = 0;
   if (tid < S) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) n_slot += s_tab[w][tid];
+  }
+  int ng = 0, nt = 0;
+  if (n_slot > 0) {
+    const bool to_tiles = (mode == LORA_MODE_SGMV) || (mode == LORA_MODE_AUTO && n_slot >= kSgmvMinTokens);
+    if (to_tiles) nt = (int)ceil_div(n_slot, kTile);
+    else ng = (int)ceil_div(n_slot, kGroup);
+    atomicMax(&s_maxlen, n_slot);
+  }
+  int4 sc = make_int4(n_slot, n_slot > 0 ? 1 : 0, ng, nt);
+  int4 tot;
+  block_exclusive_scan4(sc, s_wave_sums, tot, S);
+  const int num_active = tot.x, num_seg = tot.y, n_groups = tot.z, n_tiles = tot.w;
+  // keys 0 .. S (key S, the tokens without a slot, starts after every active
+  // token; with S = 1024 thread 0 also takes it)
+  for (int k = tid; k <= S; k += kThreads) {
+    int run = k < S ? sc.x : num_active;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = s_tab[w][k];
+      s_tab[w][k] = run;
+      run += c;
+    }
+  }
+  if (tid < S) {
+    s_count[tid] = n_slot;
     s_start[tid] = sc.x;
-    s_run[tid] = sc.x;
     s_seg[tid] = sc.y;
     s_gofs[tid] = sc.z;
     s_tofs[tid] = sc.w;
+    for (int g = 0; g < ng && sc.z + g < kItemTab; ++g) s_gslot[sc.z + g] = (int16_t)tid;
+    for (int g = 0; g < nt && sc.w + g < kItemTab; ++g) s_tslot[sc.w + g] = (int16_t)tid;
+    if (n_slot > 0) {
+      rec[L.seg_slot + sc.y] = tid;
+      rec[L.seg_start + sc.y] = sc.x;
+    }
   }
   if (tid == 0) {
-    s_gofs[S] = tot.z;
-    s_tofs[S] = tot.w;
-    s_run[S] = tot.x;  // tokens without a slot start after the active ones
-  }
-  const int num_active = tot.x, num_seg = tot.y, n_groups = tot.z, n_tiles = tot.w;
-
-  // 3. tables and info
-  if (n > 0) {
-    rec[L.seg_slot + sc.y] = tid;
-    rec[L.seg_start + sc.y] = sc.x;
-  }
-  __syncthreads();
-  if (tid == 0) {
+    s_gofs[S] = n_groups;
+    s_tofs[S] = n_tiles;
     rec[L.seg_start + num_seg] = num_active;
     rec[kNumActive] = num_active;
     rec[kNumSegments] = num_seg;
-    rec[kMaxSegLen] = s_maxlen;
     rec[kStatus] = s_bad ? LORA_ERR_INDEX : LORA_OK;
     rec[kNumGroups] = n_groups;
     rec[kNumTiles] = n_tiles;
@@ -234,52 +244,73 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
     rec[kBuiltS] = S;
     for (int w = 8; w < kInfoWords; ++w) rec[w] = 0;
   }
+  lds_barrier();
+  if (tid == 0) rec[kMaxSegLen] = s_maxlen;
 
-  // 4. stable scatter into perm (and its LDS mirror)
+  // 3. stable scatter: each wave only touches its own row of s_tab
+  auto place_chunk = [&](int t, int k, uint64_t peers) {
+    const bool valid = t < T;
+    int base = 0;
+    if (valid) base = s_tab[wave][k];  // every lane of the key reads before its first lane writes
+    if (valid && (peers & lt_mask) == 0) s_tab[wave][k] = base + __popcll(peers);
+    if (valid) {
+      const int pos = base + __popcll(peers & lt_mask);
+      perm[pos] = t;
+      if (pos < kLdsPerm) s_perm[pos] = t;
+    }
+  };
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c)
-    if (c * kThreads < T)
-      scatter_chunk(c * kThreads + tid, my_idx[c], T, S, perm, s_perm, s_run, s_wtab, s_leader_base);
-  for (int c0 = kRegChunks * kThreads; c0 < T; c0 += kThreads) {
-    const int t = c0 + tid;
-    scatter_chunk(t, t < T ? idx[t] : -1, T, S, perm, s_perm, s_run, s_wtab, s_leader_base);
+    if (c < n_chunks) place_chunk(t_begin + c * 64 + lane, key[c], peers_reg[c]);
+  for (int c = kRegChunks; c < n_chunks; ++c) {
+    const int t = t_begin + c * 64 + lane;
+    int k = t < T ? idx[t] : -1;
+    if (!(k >= 0 && k < S)) k = S;
+    place_chunk(t, k, wave_peers(k, t < T, nbits));
   }
-  if (T > kLdsPerm) __threadfence();  // the items below read perm back from global memory
-  __syncthreads();
+  if (T > kLdsPerm) {
+    __threadfence();  // the items below read perm back from global memory
+    __syncthreads();
+  } else {
+    lds_barrier();
+  }
 
-  // 5. work items: header, then the item's tokens inline (-1 past the count)
+  // 4. work items: header, then the item's tokens inline (-1 past the count)
   auto perm_at = [&](int pos) -> int {
     if (pos < kLdsPerm) return s_perm[pos];
     return __hip_atomic_load(perm + pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  for (int e = tid; e < n_groups * kGroupItemWords; e += kThreads) {
-    const int i = e / kGroupItemWords, wd = e - i * kGroupItemWords;
-    const int s = upper_slot(s_gofs, S, i);
-    const int g = i - s_gofs[s];
-    const int p0 = s_start[s] + g * kGroup;
-    const int cnt = min(kGroup, s_count[s] - g * kGroup);
-    int v;
-    if (wd == 0) v = p0;
-    else if (wd == 1) v = cnt;
-    else if (wd == 2) v = s;
-    else if (wd == 3) v = s_seg[s];
-    else v = (wd - 4 < cnt) ? perm_at(p0 + wd - 4) : -1;
-    rec[L.groups + e] = v;
-  }
-  for (int e = tid; e < n_tiles * kTileItemWords; e += kThreads) {
-    const int i = e / kTileItemWords, wd = e - i * kTileItemWords;
-    const int s = upper_slot(s_tofs, S, i);
-    const int g = i - s_tofs[s];
-    const int p0 = s_start[s] + g * kTile;
-    const int cnt = min(kTile, s_count[s] - g * kTile);
-    int v;
-    if (wd == 0) v = p0;
-    else if (wd == 1) v = cnt;
-    else if (wd == 2) v = s;
-    else if (wd == 3) v = s_seg[s];
-    else v = (wd - 4 < cnt) ? perm_at(p0 + wd - 4) : -1;
-    rec[L.tiles + e] = v;
-  }
+  // Each thread takes four words at a time, so that their chains of LDS
+  // lookups overlap.
+  auto write_items = [&](int n_items, auto words_c, int cap, const int* s_ofs, const int16_t* s_islot, int64_t at) {
+    constexpr int words = decltype(words_c)::value;  // a constant: the divisions below are multiplies
+    const int total = n_items * words;
+    for (int e0 = tid; e0 < total; e0 += 4 * kThreads) {
+      int val[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kThreads;
+        const int ec = e < total ? e : 0;
+        const int i = ec / words, wd = ec - i * words;
+        const int s = i < kItemTab ? (int)s_islot[i] : upper_slot(s_ofs, S, i);
+        const int g = i - s_ofs[s];
+        const int p0 = s_start[s] + g * cap;
+        const int cnt = min(cap, s_count[s] - g * cap);
+        int v;
+        if (wd == 0) v = p0;
+        else if (wd == 1) v = cnt;
+        else if (wd == 2) v = s;
+        else if (wd == 3) v = s_seg[s];
+        else v = (wd - 4 < cnt) ? perm_at(p0 + wd - 4) : -1;
+        val[u] = v;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e0 + u * kThreads < total) rec[at + e0 + u * kThreads] = val[u];
+    }
+  };
+  write_items(n_groups, std::integral_constant<int, kGroupItemWords>{}, kGroup, s_gofs, s_gslot, L.groups);
+  write_items(n_tiles, std::integral_constant<int, kTileItemWords>{}, kTile, s_tofs, s_tslot, L.tiles);
 }
 
 }  // namespace

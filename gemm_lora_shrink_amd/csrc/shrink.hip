@@ -205,25 +205,27 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
   for (; issued < my_n && issued < DEPTH; ++issued) issue(issued);
   for (int i = 0; i < my_n; ++i) {
     wait_vm<IPB>((issued - i - 1) * IPB);  // batch i has landed
+    // the whole batch moves to registers, so that its slot can be refilled
+    // before the multiplications
     const char* slot = ring + (i % DEPTH) * kSlot;
+    u32x4 op[2][NBLK];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      u32x4 op[NBLK];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int bk = 0; bk < NBLK; ++bk) op[bk] = *reinterpret_cast<const u32x4*>(slot + bk * kBlockBytes + rd[j]);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = M::mma(op[rb], op[RB + nb], acc[rb][nb]);
-    }
-    // the slot is refilled only after its reads are done
+      for (int bk = 0; bk < NBLK; ++bk) op[j][bk] = *reinterpret_cast<const u32x4*>(slot + bk * kBlockBytes + rd[j]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     if (issued < my_n) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(issued);
       ++issued;
     }
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = M::mma(op[j][rb], op[j][RB + nb], acc[rb][nb]);
   }
 
   // the batch that reaches past the end of D or of the part (at most one):
