@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
     ap.add_argument("--eager", action="store_true", help="time host launches instead of graph replay")
+    ap.add_argument("--no-calls", action="store_true",
+                    help="skip the per-call timing (counter runs: kernels then run in step order only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle's CPU timing (0 disables it)")
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
@@ -302,6 +304,11 @@ def main():
 
     calls = {}
     alg = [algorithmic(p) for p in problems]
+    if args.no_calls:
+        print(json.dumps(dict(metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
+                              warmup=args.warmup, ms_per_step=round(ms_per_step, 6), timed_mode=timed_mode,
+                              config=dict(workload=args.workload), calls=None)), flush=True)
+        return
     calls["segments"] = dict(us=call_time_us(do_segments), bytes=segment_bytes(T, alg[0]["n_active"]),
                              flops=0)
     if active:

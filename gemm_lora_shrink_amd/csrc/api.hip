@@ -55,18 +55,6 @@ bool gather_expand_on_valu() {
   return valu;
 }
 
-// Kernel used for the shrink of segmented tiles of 16-bit data.  By default the
-// one shrink launch covers them; LORA_MI355X_TILE_SHRINK=lds runs them in a
-// second launch whose workgroups share the slot's A chunk through LDS (kept for
-// comparison measurements).
-bool tile_shrink_on_lds() {
-  static const bool lds = [] {
-    const char* e = getenv("LORA_MI355X_TILE_SHRINK");
-    return e && strcmp(e, "lds") == 0;
-  }();
-  return lds;
-}
-
 lora_status check_common(int dt, int32_t T, int32_t n_slices, int32_t S, int32_t r_max, const void* seg) {
   if (!valid_dtype(dt)) return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", dt);
   if (T < 0) return fail(LORA_ERR_INVALID_ARG, "T = %d is negative", T);
@@ -225,15 +213,10 @@ LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, i
   p.n_slices = n_slices;
   p.T = T;
 
-  // v is written in full by the shrink launch (rows of tokens without an
-  // adapter are cleared by it), so nothing is cleared beforehand
-  const bool split_tiles = dt != LORA_F32 && tile_shrink_on_lds();
-  hipError_t e = launch_shrink(dt, p, /*groups=*/true, /*tiles=*/!split_tiles, stream);
+  // One launch shrinks every work item and leaves v fully written (preceded by
+  // a clearing launch when items are cut into parts summed with atomics).
+  const hipError_t e = launch_shrink(dt, p, /*groups=*/true, /*tiles=*/true, stream);
   if (e != hipSuccess) return hip_fail(e, "shrink launch");
-  if (split_tiles) {
-    e = launch_sgmv_shrink(dt, p, stream);
-    if (e != hipSuccess) return hip_fail(e, "segmented shrink launch");
-  }
   return LORA_OK;
 }
 

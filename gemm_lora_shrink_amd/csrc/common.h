@@ -286,9 +286,6 @@ hipError_t launch_shrink(lora_dtype dt, const ShrinkParams& p, bool groups, bool
 // v[0 .. n) = 0
 hipError_t launch_fill_zero(float* v, int64_t n, hipStream_t stream);
 hipError_t launch_bgmv_expand(lora_dtype dt, const ExpandParams& p, bool tiles, hipStream_t stream);
-// Shrink of the segmented tiles with the slot's A chunk shared through LDS
-// (16-bit types only).
-hipError_t launch_sgmv_shrink(lora_dtype dt, const ShrinkParams& p, hipStream_t stream);
 // Matrix-core expand over the gather groups and/or the segmented tiles, in one
 // launch (16-bit types only).
 hipError_t launch_mfma_expand(lora_dtype dt, const ExpandParams& p, bool groups, bool tiles, hipStream_t stream);

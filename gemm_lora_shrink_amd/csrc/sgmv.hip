@@ -1,23 +1,13 @@
-// Segmented path (SGMV) on the matrix cores: per slot segment the shrink and
-// the expand are dense contractions, so they run on v_mfma_f32_16x16x32
-// (bf16 or fp16 inputs, fp32 accumulation).  The gather kernel is not efficient
-// for prefill, and the earlier segmented kernel lost accuracy by keeping the
+// Expand on the matrix cores, for the gather groups and the segmented tiles of
+// 16-bit data: per item the expand is a dense [cnt x r] by [r x out]
+// contraction, run on v_mfma_f32_16x16x32 (bf16 or fp16 inputs, fp32
+// accumulation).  The earlier segmented kernel lost accuracy by keeping the
 // intermediate in half precision ("Add multi-LoRA support", Limitations); here
 // the intermediate stays fp32 end to end.
 //
 // MFMA 16x16x32 lane layout (checked on gfx950): for D = A(16x32) * B(32x16),
 // lane l holds A[l%16][8*(l/16) + i], B[8*(l/16) + i][l%16] (i < 8) and
 // D[4*(l/16) + i][l%16] (i < 4).
-//
-// Shrink (tiles of up to 64 tokens of one slot, one slice per workgroup):
-//   D[token][rank] = sum_d x[token][d] * A[s][rank][d].  Wave w owns tokens
-//   16w..16w+15 and all ranks.  x rows are gathered straight from global memory
-//   into the A-operand registers (each lane loads 128 contiguous bytes of its
-//   row per 256-element chunk; the contraction index is permuted identically on
-//   both operands).  The slot's A chunk (64 ranks x 256) is shared by the four
-//   waves through LDS, double-buffered, with rows padded by 16 bytes so the
-//   operand reads are conflict-free.  One barrier per chunk; the next chunk's
-//   global loads are in flight while the current one is multiplied.
 //
 // Expand (work items of up to 16 or 64 tokens):
 //   y^T[j][token] += sum_k B[s][j][k] * v[token][k] -- the transposed product,
@@ -444,129 +434,6 @@ __global__ __launch_bounds__(kThreads, 3) void mfma_expand_kernel(ExpandParams p
   }
 }
 
-// ---------------------------------------------------------------------------
-// Shrink
-// ---------------------------------------------------------------------------
-constexpr int kKC = 256;             // contraction elements per chunk
-constexpr int kLdsRow = kKC + 8;     // padded LDS row (elements)
-constexpr int kSteps = kKC / 32;     // MFMA steps per chunk
-
-template <typename Elem>
-__global__ __launch_bounds__(kThreads) void mfma_shrink_kernel(ShrinkParams p) {
-  using M = Mfma<Elem>;
-  using V = typename M::vec;
-  __shared__ __attribute__((aligned(16))) Elem s_a[2][kTile][kLdsRow];
-  __shared__ int s_tok[kTile];
-
-  // work list: (tile, slice), slice fastest, so the slices of one tile share
-  // its x rows and the tiles of one slot share its A rows in one L2
-  const SegLayout L = seg_layout(p.T, p.S);
-  const int64_t n_tiles = record_items(p.rec, p.T, p.S, true);
-  const WorkRange R = xcd_work_range(n_tiles * p.n_slices);
-  const int tid = threadIdx.x;
-
-  for (int64_t w = R.begin; w < R.end; w += R.step) {
-  const int64_t tile = w / p.n_slices;
-  const int slice = (int)(w - tile * p.n_slices);
-  Item it;
-  if (!read_item(p.rec, p.T, p.S, true, tile, it)) continue;
-  const int s = it.slot;
-  const int r = slot_rank(p.ranks, s, p.r_max);
-  if (r == 0) continue;
-
-  if (tid < kTile) s_tok[tid] = item_token(p.rec, p.T, p.S, true, tile, tid, it.cnt);
-  __syncthreads();
-
-  const int wave = tid >> 6, lane = tid & 63;
-  const int m = lane & 15, kg = lane >> 4;
-  const int tok = s_tok[wave * 16 + m];
-  const Elem* xrow = reinterpret_cast<const Elem*>(p.x) + (int64_t)(tok >= 0 ? tok : 0) * p.ldx;
-  const Elem* As = reinterpret_cast<const Elem*>(p.A[slice]) + (int64_t)s * p.r_max * p.D;
-
-  // x: MFMA step j of a chunk takes elements 32 j + 8 kg .. +7 of the lane's
-  // row, so the four lanes of a row read 64 contiguous bytes per load.
-  // A: 16-byte piece q = j * 256 + tid of the chunk is row q / 32, piece q % 32,
-  // so each wave-wide load reads 1 KB of consecutive memory.
-  u32x4 xcur[kSteps], xnext[kSteps];
-  u32x4 ar[kSteps];
-  auto load_x = [&](int c, u32x4 (&xdst)[kSteps]) {
-    const int d0 = c * kKC;
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) {
-      const int dx = d0 + 32 * j + 8 * kg;
-      const bool ok = tok >= 0 && dx < p.D;
-      xdst[j] = ld16_or0(xrow + (ok ? dx : 0), ok);
-    }
-  };
-  auto load_a = [&](int c) {
-    const int d0 = c * kKC;
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) {
-      const int q = j * kThreads + tid;
-      const int row = q >> 5, da = d0 + (q & 31) * 8;
-      const bool ok = row < r && da < p.D;
-      ar[j] = ld16_or0(As + (ok ? (int64_t)row * p.D + da : 0), ok);
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) {
-      const int q = j * kThreads + tid;
-      *reinterpret_cast<u32x4*>(&s_a[buf][q >> 5][(q & 31) * 8]) = ar[j];
-    }
-  };
-
-  f32x4 acc[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int n_chunks = (p.D + kKC - 1) / kKC;
-  load_x(0, xcur);
-  load_a(0);
-  store_a(0);
-  __syncthreads();
-  for (int c = 0; c < n_chunks; ++c) {
-    const int cur = c & 1;
-    const bool more = c + 1 < n_chunks;
-    if (more) {
-      load_x(c + 1, xnext);
-      load_a(c + 1);
-    }
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) {
-      const V xo = as_vec<V>(xcur[j]);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const V ao = as_vec<V>(*reinterpret_cast<const u32x4*>(&s_a[cur][nb * 16 + m][32 * j + 8 * kg]));
-        acc[nb] = M::mma(xo, ao, acc[nb]);
-      }
-    }
-    if (more) {
-      store_a(cur ^ 1);
-#pragma unroll
-      for (int j = 0; j < kSteps; ++j) xcur[j] = xnext[j];
-    }
-    __syncthreads();
-  }
-
-  // D[token row 4*kg + i][rank 16*nb + m] -> v
-  const float sc = p.scale ? p.scale[s] : 1.0f;
-  float* vout = p.v + (int64_t)slice * p.v_slice_stride;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = s_tok[wave * 16 + kg * 4 + i];
-    if (t < 0) continue;
-    float* vrow = vout + (int64_t)t * p.r_max;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int k = nb * 16 + m;
-      if (k < p.r_max) vrow[k] = k < r ? acc[nb][i] * sc : 0.f;
-    }
-  }
-  __syncthreads();  // the next work item reuses s_tok and s_a
-  }
-}
-
 template <typename Elem>
 hipError_t expand_launch(const ExpandParams& p, bool groups, bool tiles, hipStream_t stream) {
   const SegLayout L = seg_layout(p.T, p.S);
@@ -581,24 +448,7 @@ hipError_t expand_launch(const ExpandParams& p, bool groups, bool tiles, hipStre
   return hipGetLastError();
 }
 
-template <typename Elem>
-hipError_t shrink_launch(const ShrinkParams& p, hipStream_t stream) {
-  const SegLayout L = seg_layout(p.T, p.S);
-  const int grid = persistent_grid(reinterpret_cast<const void*>(&mfma_shrink_kernel<Elem>), kThreads, 0,
-                                   L.cap_tiles * p.n_slices);
-  hipLaunchKernelGGL(mfma_shrink_kernel<Elem>, dim3(grid), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
 }  // namespace
-
-hipError_t launch_sgmv_shrink(lora_dtype dt, const ShrinkParams& p, hipStream_t stream) {
-  switch (dt) {
-    case LORA_F16: return shrink_launch<half_t>(p, stream);
-    case LORA_BF16: return shrink_launch<bf16_t>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
 
 hipError_t launch_mfma_expand(lora_dtype dt, const ExpandParams& p, bool groups, bool tiles, hipStream_t stream) {
   switch (dt) {
