@@ -417,8 +417,12 @@ hipError_t launch(const ShrinkParams& p, bool groups, bool tiles, hipStream_t st
   const int resident = persistent_grid(kernel, kThreads, 0, INT64_MAX / 4);
   const int n_steps = (int)ceil_div(p.D, 4 * Traits<Elem>::kVec);
   const int64_t target = resident * 3 / 4;
-  const int parts_t = tiles ? parts_for(L.cap_tiles * p.n_slices, n_steps, target) : 0;
   const int parts_g = groups ? parts_for(L.cap_groups * p.n_slices, n_steps, target) : 0;
+  // Tiles are cut into parts only when the groups already need v cleared: the
+  // tile list's capacity counts a ragged tile for every slot, so it is mostly
+  // empty in decode-shaped batches, and a clearing launch it alone asked for
+  // would usually be wasted.
+  const int parts_t = tiles ? (parts_g > 1 || !groups ? parts_for(L.cap_tiles * p.n_slices, n_steps, target) : 1) : 0;
   const bool cleared = parts_t > 1 || parts_g > 1;
   if (cleared) {
     // partial sums are added into v: clear it first (this also clears the
