@@ -191,8 +191,9 @@ __device__ inline void expand_columns(const ExpandParams& p, const int* s_tok, c
 }
 
 // A gather group (at most 16 tokens) needs no shared staging: each wave loads
-// its own v operands, so a unit costs two memory round trips -- the item
-// (header and tokens), then its y, B and v together -- and no workgroup barrier.
+// its own v operands (once per unit, with the first column tile's y and B
+// rows) and then walks its column tiles with the next tile's y and B rows in
+// flight while the current tile is multiplied -- no workgroup barrier.
 template <typename Elem>
 __device__ inline void expand_group_direct(const ExpandParams& p, const int32_t* ip, const Item& it,
                                            float (*s_tr)[16][kTrRow], int slice, int s, int r, int out,
@@ -217,85 +218,89 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const int32_t*
   Elem* ybase = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + yc;
   const float* vrow = p.v + (int64_t)slice * p.v_slice_stride + (int64_t)(tok_n >= 0 ? tok_n : 0) * p.r_max;
 
-  for (int ct = ct_begin; ct < ct_end; ++ct) {
+  // y pieces and B rows of column tile ct (zeros past ct_end: the last
+  // prefetch issues only loads of the zero constant)
+  auto load_tile = [&](int ct, u32x4 (&yd)[2], u32x4 (&bd)[4][2]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
-    const bool ycol_ok = jw + yc < out;  // out is a multiple of 8
-    // y, B and (first tile) v requests go out together
-    u32x4 yold[2];
-    yold[0] = ld16_or0(ycol_ok && ytok0 >= 0 ? ybase + jw + (int64_t)ytok0 * p.ldy : yzero, ycol_ok && ytok0 >= 0);
-    yold[1] = ld16_or0(ycol_ok && ytok1 >= 0 ? ybase + jw + (int64_t)ytok1 * p.ldy : yzero, ycol_ok && ytok1 >= 0);
-    u32x4 braw[4][2];
+    const bool ycol_ok = ct < ct_end && jw + yc < out;  // out is a multiple of 8
+    yd[0] = ld16_or0(ycol_ok && ytok0 >= 0 ? ybase + jw + (int64_t)ytok0 * p.ldy : yzero, ycol_ok && ytok0 >= 0);
+    yd[1] = ld16_or0(ycol_ok && ytok1 >= 0 ? ybase + jw + (int64_t)ytok1 * p.ldy : yzero, ycol_ok && ytok1 >= 0);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int row = jw + cb * 16 + n;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int k0 = ks * 32 + kg * 8;
-        const bool ok = ks < nks && row < out && k0 < r;
-        braw[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok);
+        const bool ok = ct < ct_end && ks < nks && row < out && k0 < r;
+        bd[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok);
       }
     }
-    f32x4 vraw[2][2];
+  };
+  u32x4 ya[2], ba[4][2], yb[2], bb[4][2];
+  load_tile(ct_begin, ya, ba);
+
+  // the group's v operands, once per unit
+  f32x4 vraw[2][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int k0 = ks * 32 + kg * 8;
-      const bool ok = tok_n >= 0 && ks < nks && k0 < r;
-      vraw[ks][0] = ldf4_or0(vrow + (ok ? k0 : 0), ok);
-      vraw[ks][1] = ldf4_or0(vrow + (ok ? k0 + 4 : 0), ok);
+  for (int ks = 0; ks < 2; ++ks) {
+    const int k0 = ks * 32 + kg * 8;
+    const bool ok = tok_n >= 0 && ks < nks && k0 < r;
+    vraw[ks][0] = ldf4_or0(vrow + (ok ? k0 : 0), ok);
+    vraw[ks][1] = ldf4_or0(vrow + (ok ? k0 + 4 : 0), ok);
+  }
+  float vv[2][8];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int k0 = ks * 32 + kg * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vv[ks][i] = (k0 + i < r) ? vraw[ks][0][i] : 0.f;
+      vv[ks][4 + i] = (k0 + 4 + i < r) ? vraw[ks][1][i] : 0.f;
     }
-    V bop[4][2];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        bop[cb][ks] = as_vec<V>(ragged_rank ? mask_tail16(braw[cb][ks], ks * 32 + kg * 8, r) : braw[cb][ks]);
-    float vv[2][8];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int k0 = ks * 32 + kg * 8;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vv[ks][i] = (k0 + i < r) ? vraw[ks][0][i] : 0.f;
-        vv[ks][4 + i] = (k0 + 4 + i < r) ? vraw[ks][1][i] : 0.f;
-      }
-    }
-    float unscale = 1.0f;
-    if constexpr (Tr::kDtype == LORA_F16) {
-      float mx = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(vv[ks][i]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (mx > 0.f) {
-        int ex;
-        frexpf(mx, &ex);
-        const float sc = ldexpf(1.0f, 1 - ex);
-        unscale = ldexpf(1.0f, ex - 1);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) vv[ks][i] *= sc;
-      }
-    }
-    V vhi[2], vlo[2];
+  }
+  float unscale = 1.0f;
+  if constexpr (Tr::kDtype == LORA_F16) {
+    float mx = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const Elem h = static_cast<Elem>(vv[ks][i]);
-        vhi[ks][i] = h;
-        vlo[ks][i] = static_cast<Elem>(vv[ks][i] - static_cast<float>(h));
-      }
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(vv[ks][i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx > 0.f) {
+      int ex;
+      frexpf(mx, &ex);
+      const float sc = ldexpf(1.0f, 1 - ex);
+      unscale = ldexpf(1.0f, ex - 1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vv[ks][i] *= sc;
+    }
+  }
+  V vhi[2], vlo[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const Elem h = static_cast<Elem>(vv[ks][i]);
+      vhi[ks][i] = h;
+      vlo[ks][i] = static_cast<Elem>(vv[ks][i] - static_cast<float>(h));
+    }
+
+  auto compute_tile = [&](int ct, const u32x4 (&yd)[2], const u32x4 (&bd)[4][2]) {
+    const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
+    const bool ycol_ok = jw + yc < out;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
+      V b0 = as_vec<V>(ragged_rank ? mask_tail16(bd[cb][0], kg * 8, r) : bd[cb][0]);
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc = M::mma(bop[cb][0], vhi[0], acc);
-      acc = M::mma(bop[cb][0], vlo[0], acc);
+      acc = M::mma(b0, vhi[0], acc);
+      acc = M::mma(b0, vlo[0], acc);
       if (nks > 1) {
-        acc = M::mma(bop[cb][1], vhi[1], acc);
-        acc = M::mma(bop[cb][1], vlo[1], acc);
+        V b1 = as_vec<V>(ragged_rank ? mask_tail16(bd[cb][1], 32 + kg * 8, r) : bd[cb][1]);
+        acc = M::mma(b1, vhi[1], acc);
+        acc = M::mma(b1, vlo[1], acc);
       }
       if constexpr (Tr::kDtype == LORA_F16) acc *= unscale;
       *reinterpret_cast<f32x4*>(&s_tr[wave][n][cb * 16 + kg * 4]) = acc;
@@ -313,7 +318,7 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const int32_t*
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t wd = yold[h][q];
+          const uint32_t wd = yd[h][q];
           const float y0 = Tr::elem_to_float(wd & 0xffffu) + add[2 * q];
           const float y1 = Tr::elem_to_float(wd >> 16) + add[2 * q + 1];
           if constexpr (Tr::kDtype == LORA_BF16) o[q] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
@@ -325,6 +330,15 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const int32_t*
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // two tiles per iteration, so that the register buffers alternate without copies
+  for (int ct = ct_begin; ct < ct_end; ct += 2) {
+    load_tile(ct + 1, yb, bb);
+    compute_tile(ct, ya, ba);
+    if (ct + 1 >= ct_end) break;
+    load_tile(ct + 2, ya, ba);
+    compute_tile(ct + 1, yb, bb);
   }
 }
 
