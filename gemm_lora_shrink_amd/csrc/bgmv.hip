@@ -47,11 +47,11 @@ __device__ inline void store_y4(Elem* dst, const float* acc, typename YChunk<Ele
     const float y3 = Tr::elem_to_float(w1 >> 16) + acc[3];
     u32x2 o;
     if constexpr (Tr::kDtype == LORA_BF16) {
-      o[0] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
-      o[1] = float_to_bf16_bits(y2) | (float_to_bf16_bits(y3) << 16);
+      o[0] = pack2_bf16(y0, y1);
+      o[1] = pack2_bf16(y2, y3);
     } else {
-      o[0] = float_to_f16_bits(y0) | (float_to_f16_bits(y1) << 16);
-      o[1] = float_to_f16_bits(y2) | (float_to_f16_bits(y3) << 16);
+      o[0] = pack2_f16(y0, y1);
+      o[1] = pack2_f16(y2, y3);
     }
     *reinterpret_cast<u32x2*>(dst) = o;
   }

@@ -84,6 +84,16 @@ __device__ inline uint32_t float_to_f16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<half_t>(f));
 }
 
+// Two fp32 values rounded to nearest-even into one word of two 16-bit lanes
+// (a in the low half): one packed conversion instruction on gfx950.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ inline uint32_t pack2_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
 // Reinterpret one 32-bit word as two 16-bit lanes.  The word is always passed
 // by value: this compiler mis-lowers __builtin_bit_cast applied directly to an
 // element of an ext_vector (it reads element 0 whatever the index), so vector

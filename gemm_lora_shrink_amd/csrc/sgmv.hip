@@ -152,7 +152,7 @@ __device__ inline void expand_columns(const ExpandParams& p, const int* s_tok, c
           acc = M::mma(bop[cb][1], vhi[1], acc);
           acc = M::mma(bop[cb][1], vlo[1], acc);
         }
-        acc *= unscale;
+        if constexpr (Tr::kDtype == LORA_F16) acc *= unscale;  // bf16 rows are not scaled
         *reinterpret_cast<f32x4*>(&s_tr[wave][n][cb * 16 + kg * 4]) = acc;
       }
       // the block is written and read by this wave only
@@ -172,8 +172,8 @@ __device__ inline void expand_columns(const ExpandParams& p, const int* s_tok, c
             const uint32_t wd = yold[sb][h][q];
             const float y0 = Tr::elem_to_float(wd & 0xffffu) + add[2 * q];
             const float y1 = Tr::elem_to_float(wd >> 16) + add[2 * q + 1];
-            if constexpr (Tr::kDtype == LORA_BF16) o[q] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
-            else o[q] = float_to_f16_bits(y0) | (float_to_f16_bits(y1) << 16);
+            if constexpr (Tr::kDtype == LORA_BF16) o[q] = pack2_bf16(y0, y1);
+            else o[q] = pack2_f16(y0, y1);
           }
           *reinterpret_cast<u32x4*>(ybase + jw + (int64_t)t * p.ldy) = o;
         }
@@ -321,8 +321,8 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const int32_t*
           const uint32_t wd = yd[h][q];
           const float y0 = Tr::elem_to_float(wd & 0xffffu) + add[2 * q];
           const float y1 = Tr::elem_to_float(wd >> 16) + add[2 * q + 1];
-          if constexpr (Tr::kDtype == LORA_BF16) o[q] = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
-          else o[q] = float_to_f16_bits(y0) | (float_to_f16_bits(y1) << 16);
+          if constexpr (Tr::kDtype == LORA_BF16) o[q] = pack2_bf16(y0, y1);
+          else o[q] = pack2_f16(y0, y1);
         }
         *reinterpret_cast<u32x4*>(ybase + jw + (int64_t)t * p.ldy) = o;
       }
