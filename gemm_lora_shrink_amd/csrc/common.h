@@ -101,6 +101,11 @@ __device__ inline uint32_t pack2_f16(float a, float b) {
 __device__ inline f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ inline bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its global loads and stores (__syncthreads also waits
+// for those).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Branch-free guarded loads.  A lane whose access is out of range reads 16
 // bytes of zeros from a small constant array instead, so the select is on the
 // address, before the load: no branch splits the code (the compiler would wait
@@ -263,7 +268,10 @@ __device__ inline const int32_t* item_ptr(const int32_t* rec, int T, int S, bool
 // Header of item `i` (< record_items) of a list, with its fields checked
 // against the sizes.
 __device__ inline bool read_item(const int32_t* rec, int T, int S, bool tiles, int64_t i, Item& it) {
-  it = *reinterpret_cast<const Item*>(item_ptr(rec, T, S, tiles, i));
+  // one 16-byte load (items are 16-byte aligned), so that the checks below
+  // do not split the header into dependent loads
+  const u32x4 h = *reinterpret_cast<const u32x4*>(item_ptr(rec, T, S, tiles, i));
+  it = Item{(int)h[0], (int)h[1], (int)h[2], (int)h[3]};
   const int cap = tiles ? kTile : kGroup;
   return it.slot >= 0 && it.slot < S && it.p0 >= 0 && it.cnt > 0 && it.cnt <= cap && it.p0 + it.cnt <= T;
 }

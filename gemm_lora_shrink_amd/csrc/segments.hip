@@ -42,11 +42,8 @@ constexpr int kItemTab = 2048;  // items whose slot is tabulated in LDS
 
 __device__ inline int lane_id() { return __lane_id(); }
 
-// Workgroup barrier for data exchanged through LDS only.  __syncthreads() also
-// orders global memory, so it waits for every outstanding global store (the
-// perm and table writes) first; here only this wave's LDS operations are
-// waited for.
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Barriers here are lds_barrier(): __syncthreads() would also wait for every
+// outstanding global store (the perm and table writes).
 
 // Lanes of this wave (valid ones only) whose key equals this lane's: one ballot
 // per bit of the key, keys being below 2^nbits; a chunk whose valid lanes all

@@ -40,21 +40,17 @@ template <> struct Mfma<half_t> {
   }
 };
 
-__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
 template <typename V> __device__ inline V as_vec(u32x4 u) { return __builtin_bit_cast(V, u); }
 
-// Zero the 16-bit elements k0 + e (e < 8) that are >= r.
+// Zero the 16-bit elements k0 + e (e < 8) that are >= r.  Selects only: a
+// branch here would make the compiler wait for the load that produced u
+// before issuing the loads that follow it.
 __device__ inline u32x4 mask_tail16(u32x4 u, int k0, int r) {
-  if (k0 + 8 <= r) return u;
-  if (k0 >= r) return u32x4{0, 0, 0, 0};
   u32x4 o;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const uint32_t word = u[w];
-    const uint32_t lo = (k0 + 2 * w < r) ? (word & 0xffffu) : 0u;
-    const uint32_t hi = (k0 + 2 * w + 1 < r) ? (word & 0xffff0000u) : 0u;
-    o[w] = lo | hi;
+    const uint32_t keep = (k0 + 2 * w + 1 < r) ? 0xffffffffu : ((k0 + 2 * w < r) ? 0x0000ffffu : 0u);
+    o[w] = u[w] & keep;
   }
   return o;
 }
@@ -77,14 +73,17 @@ constexpr int kSubs = kTile / 16;                              // 16-token sub-b
 constexpr int kTrRow = kExpandColsPerWave + 4;                 // padded fp32 LDS row
 constexpr int kVRow = LORA_MAX_RANK + 8;                       // padded 16-bit LDS row of v
 
-// The column tiles [ct_begin, ct_end) of one unit: NSUB 16-token sub-blocks
-// (1 for a gather group, up to 4 for a tile; sub-blocks past the item's
-// tokens hold no token and are skipped by their -1 entries).
+// One tile unit: the column tiles [ct_begin, ct_end) of an item of up to 64
+// tokens (NSUB 16-token sub-blocks; sub-blocks past the item's tokens hold no
+// token and are skipped by their -1 entries).  tok_v is the token of this
+// thread's v row (row tid / 4, -1 past the item's count).  The v rows, the
+// first column tile's y and its B rows are all requested before any of them
+// is waited for; the fp32 v rows are then converted into the 16-bit hi/lo
+// operands in LDS.
 template <typename Elem, int NSUB>
-__device__ inline void expand_columns(const ExpandParams& p, const int* s_tok, const float* s_unscale,
-                                      const Elem (*s_vhi)[kVRow], const Elem (*s_vlo)[kVRow],
-                                      float (*s_tr)[16][kTrRow], int slice, int s, int r, int out, int ct_begin,
-                                      int ct_end) {
+__device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, int* s_tok, float* s_unscale,
+                                   Elem (*s_vhi)[kVRow], Elem (*s_vlo)[kVRow], float (*s_tr)[16][kTrRow],
+                                   int slice, int s, int r, int out, int ct_begin, int ct_end) {
   using M = Mfma<Elem>;
   using V = typename M::vec;
   using Tr = Traits<Elem>;
@@ -94,9 +93,24 @@ __device__ inline void expand_columns(const ExpandParams& p, const int* s_tok, c
   const int yr = lane >> 3, yc = (lane & 7) * 8;
   const Elem* yzero = reinterpret_cast<const Elem*>(g_zero16);
   const int nks = r > 32 ? 2 : 1;  // 32-wide rank steps
-  const int n_sub = NSUB;
+  const bool ragged_rank = (r & 7) != 0;
   const Elem* Bs = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max;
   Elem* ybase = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + yc;
+
+  // this thread's v row: token tid / 4, ranks 16 (tid % 4) .. +15
+  const int tt = tid >> 2, kq = (tid & 3) * 16;
+  if ((tid & 3) == 0) s_tok[tt] = tok_v;
+  f32x4 vraw[4];
+  {
+    const float* src = p.v + (int64_t)slice * p.v_slice_stride + (int64_t)(tok_v >= 0 ? tok_v : 0) * p.r_max + kq;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = tok_v >= 0 && kq + 4 * q < r;
+      vraw[q] = ldf4_or0(src + (ok ? 4 * q : 0), ok);
+    }
+  }
+  lds_barrier();  // s_tok is visible; the v loads stay in flight
+
   // y of every sub-block of column tile `ct`, lane-contiguous (zeros past the end)
   auto load_y = [&](int ct, u32x4 (&dst)[NSUB][2]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
@@ -110,27 +124,82 @@ __device__ inline void expand_columns(const ExpandParams& p, const int* s_tok, c
         dst[sb][h] = ld16_or0(ok ? ybase + jw + (int64_t)t * p.ldy : yzero, ok);
       }
   };
-  u32x4 yold[NSUB][2];
-  load_y(ct_begin, yold);
-  for (int ct = ct_begin; ct < ct_end; ++ct) {
+  // A operand: this wave's 64 B rows of column tile `ct` (4 blocks x 16), both
+  // rank steps; rank columns past the slot's rank are not read
+  auto load_b = [&](int ct, u32x4 (&bop)[4][2]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
-    const bool ycol_ok = jw + yc < out;  // out is a multiple of 8
-    // A operand: this wave's 64 B rows (4 blocks x 16), both rank steps.  They
-    // are requested before the next tile's y, so that waiting for them never
-    // waits for that prefetch (loads complete in order).
-    V bop[4][2];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int row = jw + cb * 16 + n;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int k0 = ks * 32 + kg * 8;
-        const bool ok = ks < nks && row < out && k0 < r;  // rank columns past the slot's rank are not read
-        bop[cb][ks] = as_vec<V>(mask_tail16(ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok), k0, r));
+        const bool ok = ks < nks && row < out && k0 < r;
+        bop[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok);
       }
     }
+  };
+  u32x4 yold[NSUB][2];
+  u32x4 bop[4][2];
+  load_y(ct_begin, yold);
+  load_b(ct_begin, bop);
+
+  {
+    float vv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[4 * q + e] = (kq + 4 * q + e < r) ? vraw[q][e] : 0.f;
+    float unscale = 1.0f;
+    if constexpr (Tr::kDtype == LORA_F16) {
+      // scale the token's row by a power of two so that |v| < 2
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(vv[e]));
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+      if (mx > 0.f) {
+        int ex;
+        frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
+        const float sc = ldexpf(1.0f, 1 - ex);
+        unscale = ldexpf(1.0f, ex - 1);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vv[e] *= sc;
+      }
+    }
+    if ((tid & 3) == 0) s_unscale[tt] = unscale;
+    V hi0, hi1, lo0, lo1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const Elem h0 = static_cast<Elem>(vv[e]), h1 = static_cast<Elem>(vv[8 + e]);
+      hi0[e] = h0;
+      hi1[e] = h1;
+      lo0[e] = static_cast<Elem>(vv[e] - static_cast<float>(h0));
+      lo1[e] = static_cast<Elem>(vv[8 + e] - static_cast<float>(h1));
+    }
+    *reinterpret_cast<V*>(&s_vhi[tt][kq]) = hi0;
+    *reinterpret_cast<V*>(&s_vhi[tt][kq + 8]) = hi1;
+    *reinterpret_cast<V*>(&s_vlo[tt][kq]) = lo0;
+    *reinterpret_cast<V*>(&s_vlo[tt][kq + 8]) = lo1;
+  }
+  lds_barrier();  // the v operands are visible; y and B loads stay in flight
+
+  for (int ct = ct_begin; ct < ct_end; ++ct) {
+    const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
+    const bool ycol_ok = jw + yc < out;  // out is a multiple of 8
+    // B rows are requested before the next tile's y, so that waiting for them
+    // never waits for that prefetch (loads complete in order)
+    if (ct > ct_begin) load_b(ct, bop);
     u32x4 ynext[NSUB][2];
     load_y(ct + 1, ynext);
+    // a rank that is not a multiple of 8 ends inside one 16-byte piece: zero
+    // the columns past it (loaded pieces past the rank are zeros already)
+    V bv[4][2];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        bv[cb][ks] = as_vec<V>(ragged_rank ? mask_tail16(bop[cb][ks], ks * 32 + kg * 8, r) : bop[cb][ks]);
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
       if (sb >= n_sub) break;
@@ -146,11 +215,11 @@ __device__ inline void expand_columns(const ExpandParams& p, const int* s_tok, c
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc = M::mma(bop[cb][0], vhi[0], acc);
-        acc = M::mma(bop[cb][0], vlo[0], acc);
+        acc = M::mma(bv[cb][0], vhi[0], acc);
+        acc = M::mma(bv[cb][0], vlo[0], acc);
         if (nks > 1) {
-          acc = M::mma(bop[cb][1], vhi[1], acc);
-          acc = M::mma(bop[cb][1], vlo[1], acc);
+          acc = M::mma(bv[cb][1], vhi[1], acc);
+          acc = M::mma(bv[cb][1], vlo[1], acc);
         }
         if constexpr (Tr::kDtype == LORA_F16) acc *= unscale;  // bf16 rows are not scaled
         *reinterpret_cast<f32x4*>(&s_tr[wave][n][cb * 16 + kg * 4]) = acc;
@@ -195,7 +264,7 @@ __device__ inline void expand_columns(const ExpandParams& p, const int* s_tok, c
 // rows) and then walks its column tiles with the next tile's y and B rows in
 // flight while the current tile is multiplied -- no workgroup barrier.
 template <typename Elem>
-__device__ inline void expand_group_direct(const ExpandParams& p, const int32_t* ip, const Item& it,
+__device__ inline void expand_group_direct(const ExpandParams& p, int tok_n, int ytok0, int ytok1,
                                            float (*s_tr)[16][kTrRow], int slice, int s, int r, int out,
                                            int ct_begin, int ct_end) {
   using M = Mfma<Elem>;
@@ -207,12 +276,6 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const int32_t*
   const int yr = lane >> 3, yc = (lane & 7) * 8;
   const int nks = r > 32 ? 2 : 1;
   const bool ragged_rank = (r & 7) != 0;
-  auto tok_at = [&](int k) -> int {
-    const int t = ip[4 + k];
-    return k < it.cnt ? (t < 0 ? 0 : (t >= p.T ? p.T - 1 : t)) : -1;
-  };
-  const int tok_n = tok_at(n);
-  const int ytok0 = tok_at(yr), ytok1 = tok_at(yr + 8);
   const Elem* Bs = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max;
   const Elem* yzero = reinterpret_cast<const Elem*>(g_zero16);
   Elem* ybase = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + yc;
@@ -342,123 +405,149 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const int32_t*
   }
 }
 
+// One unit: the column tiles [ct_begin, ct_end) of item `li` of a list
+// (tiles or gather groups) for one slice.
 template <typename Elem>
-__global__ __launch_bounds__(kThreads, 3) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles,
-                                                               int n_ct) {
-  using M = Mfma<Elem>;
-  using V = typename M::vec;
-  using Tr = Traits<Elem>;
+__device__ inline void expand_unit(const ExpandParams& p, int slice, bool tiles, int64_t li, int ct_begin,
+                                   int ct_end, int* s_tok, float* s_unscale, Elem (*s_vhi)[kVRow],
+                                   Elem (*s_vlo)[kVRow], float (*s_tr)[16][kTrRow]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int n = lane & 15, yr = lane >> 3;
+  const int out = (int)p.out_size[slice];
+  // The item's header and the token words this thread needs arrive in one
+  // memory round trip: the token of its v row (tile path: row tid / 4) and
+  // those of its MFMA column and y rows (gather path).
+  const int32_t* ip = item_ptr(p.rec, p.T, p.S, tiles, li);
+  const int tw_v = ip[4 + (tiles ? (tid >> 2) : ((tid >> 2) & (kGroup - 1)))];
+  const int tw_n = ip[4 + n], tw_y0 = ip[4 + yr], tw_y1 = ip[4 + yr + 8];
+  Item it;
+  if (!read_item(p.rec, p.T, p.S, tiles, li, it)) return;
+  const int s = it.slot;
+  const int r = slot_rank(p.ranks, s, p.r_max);
+  if (r == 0) return;
+  // token k of the item, clamped into [0, T); -1 past its count
+  auto tok = [&](int k, int t) { return k < it.cnt ? (t < 0 ? 0 : (t >= p.T ? p.T - 1 : t)) : -1; };
+  if (it.cnt <= 16) {
+    // uniform per unit; this path uses only wave-private LDS
+    expand_group_direct<Elem>(p, tok(n, tw_n), tok(yr, tw_y0), tok(yr + 8, tw_y1), s_tr, slice, s, r, out,
+                              ct_begin, ct_end);
+    return;
+  }
+  expand_tile<Elem, kSubs>(p, tok(tid >> 2, tw_v), (it.cnt + 15) >> 4, s_tok, s_unscale, s_vhi, s_vlo, s_tr,
+                           slice, s, r, out, ct_begin, ct_end);
+  lds_barrier();  // the next unit rewrites s_tok and the v operands
+}
+
+// The work is the pairs (item, 256-column tile) of every slice.  Each slice's
+// column tiles are cut into blocks of C, and the pairs are ordered by slice,
+// block, item (gather groups first), column tile.  A tile pair weighs
+// kTileWeight and a group pair 1 (a tile holds up to four times the tokens).
+// Share k of G takes the pairs whose weighted start lies in
+// [W k / G, W (k + 1) / G): a contiguous run, so that the per-item set-up
+// (tokens, v operands) is paid about once or twice per workgroup.  The shares
+// of one XCD's workgroups are adjacent.
+//   C is a whole slice (item order) unless the B rows of the slots one XCD
+// sees would not stay in its L2; then C is about the pairs per share, so that
+// the items of one slot, which read the same B rows, are in adjacent shares
+// and are taken at the same time by workgroups of one XCD.
+//   G is the grid, or the number of pairs when that is smaller (rounded up to
+// a multiple of kXcds): shares then go to the first workgroups of every XCD,
+// which the hardware places on distinct compute units.
+constexpr int kTileWeight = 4;
+constexpr int64_t kL2Bytes = 4 << 20;  // per XCD
+
+template <typename Elem>
+__global__ __launch_bounds__(kThreads, 2) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles) {
   __shared__ int s_tok[kTile];
   __shared__ float s_unscale[kTile];
   __shared__ __attribute__((aligned(16))) Elem s_vhi[kTile][kVRow];
   __shared__ __attribute__((aligned(16))) Elem s_vlo[kTile][kVRow];
   __shared__ __attribute__((aligned(16))) float s_tr[4][16][kTrRow];
 
-  const SegLayout L = seg_layout(p.T, p.S);
-  const int n_g = use_groups ? record_items(p.rec, p.T, p.S, false) : 0;
-  const int n_t = use_tiles ? record_items(p.rec, p.T, p.S, true) : 0;
-  const int64_t n_items = (int64_t)n_g + n_t;
-  // column tiles per unit: enough units to give every workgroup about two
-  const int64_t tile_slots = n_items * n_ct * p.n_slices;
-  int run = (int)(tile_slots / (2 * (int64_t)gridDim.x));
-  run = run < 1 ? 1 : (run > n_ct ? n_ct : run);
-  const int n_runs = (n_ct + run - 1) / run;
-  // unit order: item fastest, then column run, then slice
-  const WorkRange R = xcd_work_range(n_items * n_runs * p.n_slices);
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int n = lane & 15, kg = lane >> 4;
-  const int yr = lane >> 3, yc = (lane & 7) * 8;
-  const Elem* yzero = reinterpret_cast<const Elem*>(g_zero16);
-
-  for (int64_t w = R.begin; w < R.end; w += R.step) {
-  const int64_t item = w % n_items;
-  const int64_t rest = w / n_items;
-  const int cr = (int)(rest % n_runs);
-  const int slice = (int)(rest / n_runs);
-  const bool tiles = item >= n_g;
-  Item it;
-  if (!read_item(p.rec, p.T, p.S, tiles, tiles ? item - n_g : item, it)) continue;
-  const int out = (int)p.out_size[slice];
-  const int ct_begin = cr * run;
-  const int ct_end = min(ct_begin + run, (int)ceil_div(out, kExpandColsPerWG));
-  if (ct_begin >= ct_end) continue;
-  const int s = it.slot;
-  const int r = slot_rank(p.ranks, s, p.r_max);
-  if (r == 0) continue;
-  if (it.cnt <= 16) {
-    // uniform per unit; this path uses only wave-private LDS
-    expand_group_direct<Elem>(p, item_ptr(p.rec, p.T, p.S, tiles, tiles ? item - n_g : item), it, s_tr, slice,
-                              s, r, out, ct_begin, ct_end);
-    continue;
+  const int64_t n_g = use_groups ? record_items(p.rec, p.T, p.S, false) : 0;
+  const int64_t n_t = use_tiles ? record_items(p.rec, p.T, p.S, true) : 0;
+  const int64_t per_col = n_g + kTileWeight * n_t;  // weight of one column tile of every item
+  auto n_cols = [&](int i) { return (int)ceil_div(p.out_size[i], kExpandColsPerWG); };
+  int64_t W = 0, pairs = 0, max_out = 0;
+  int max_cols = 1;
+  for (int i = 0; i < p.n_slices; ++i) {
+    W += n_cols(i) * per_col;
+    pairs += n_cols(i) * (n_g + n_t);
+    max_cols = max(max_cols, n_cols(i));
+    max_out = max(max_out, p.out_size[i]);
   }
-  const int n_sub = (it.cnt + 15) >> 4;
+  // grid and pair counts are multiples of kXcds once rounded
+  const int64_t G = min((int64_t)gridDim.x, max((int64_t)kXcds, ceil_div(pairs, kXcds) * kXcds));
+  const int64_t lb = blockIdx.x / kXcds;
+  if (lb >= G / kXcds) return;  // uniform: this workgroup has no share
+  const int64_t k = (blockIdx.x % kXcds) * (G / kXcds) + lb;
+  const int64_t w0 = W * k / G, w1 = W * (k + 1) / G;
+  const int64_t n_seg = max(1, p.rec[kNumSegments]);  // distinct slots in the batch
+  const bool blocks = ceil_div(n_seg, kXcds) * max_out * p.r_max * (int64_t)sizeof(Elem) > kL2Bytes;
+  const int C = blocks ? (int)min((int64_t)max_cols, max((int64_t)1, ceil_div(pairs, G))) : max_cols;
 
-  // token list and the item's v rows as hi + lo (thread: token tid / 4,
-  // ranks 16 (tid % 4) .. +15)
-  {
-    const int tt = tid >> 2, kq = (tid & 3) * 16;
-    const int tok = item_token(p.rec, p.T, p.S, tiles, tiles ? item - n_g : item, tt, it.cnt);
-    if ((tid & 3) == 0) s_tok[tt] = tok;
-    const float* src = p.v + (int64_t)slice * p.v_slice_stride + (int64_t)(tok >= 0 ? tok : 0) * p.r_max + kq;
-    float vv[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool ok = tok >= 0 && kq + 4 * q < p.r_max;
-      const f32x4 f = ldf4_or0(src + (ok ? 4 * q : 0), ok);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vv[4 * q + e] = (kq + 4 * q + e < r) ? f[e] : 0.f;
+  // blocks in order: (slice, first column tile c0, width cb); base is the
+  // block's weighted start
+  int slice = 0, c0 = 0;
+  int64_t base = 0;
+  auto width = [&]() { return min(C, n_cols(slice) - c0); };
+  auto next_block = [&]() {
+    base += width() * per_col;
+    c0 += C;
+    if (c0 >= n_cols(slice)) {
+      c0 = 0;
+      ++slice;
     }
-    float unscale = 1.0f;
-    if constexpr (Tr::kDtype == LORA_F16) {
-      // scale the token's row by a power of two so that |v| < 2
-      float mx = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(vv[e]));
-      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-      if (mx > 0.f) {
-        int ex;
-        frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
-        const float sc = ldexpf(1.0f, 1 - ex);
-        unscale = ldexpf(1.0f, ex - 1);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) vv[e] *= sc;
-      }
+  };
+  // the first pair whose weighted start is >= w0
+  while (slice < p.n_slices && base + width() * per_col <= w0) next_block();
+  int64_t item = 0;
+  int ct = 0;  // column tile within the block
+  if (slice < p.n_slices) {
+    const int cb = width();
+    const int64_t rel = w0 - base;
+    if (rel < n_g * cb) {
+      item = rel / cb;
+      ct = (int)(rel % cb);
+    } else {
+      const int64_t q = ceil_div(rel - n_g * cb, kTileWeight);
+      item = n_g + q / cb;
+      ct = (int)(q % cb);
     }
-    if ((tid & 3) == 0) s_unscale[tt] = unscale;
-    V hi0, hi1, lo0, lo1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const Elem h0 = static_cast<Elem>(vv[e]), h1 = static_cast<Elem>(vv[8 + e]);
-      hi0[e] = h0;
-      hi1[e] = h1;
-      lo0[e] = static_cast<Elem>(vv[e] - static_cast<float>(h0));
-      lo1[e] = static_cast<Elem>(vv[8 + e] - static_cast<float>(h1));
-    }
-    *reinterpret_cast<V*>(&s_vhi[tt][kq]) = hi0;
-    *reinterpret_cast<V*>(&s_vhi[tt][kq + 8]) = hi1;
-    *reinterpret_cast<V*>(&s_vlo[tt][kq]) = lo0;
-    *reinterpret_cast<V*>(&s_vlo[tt][kq + 8]) = lo1;
   }
-  __syncthreads();
-
-  expand_columns<Elem, kSubs>(p, s_tok, s_unscale, s_vhi, s_vlo, s_tr, slice, s, r, out, ct_begin, ct_end);
-  __syncthreads();  // the next unit rewrites s_tok and the v operands
+  while (slice < p.n_slices) {
+    const int cb = width();
+    if (item >= n_g + n_t) {  // past the block's last item
+      next_block();
+      item = 0;
+      ct = 0;
+      continue;
+    }
+    const bool tiles = item >= n_g;
+    const int64_t pos = base + (tiles ? n_g * cb + kTileWeight * ((item - n_g) * cb + ct) : item * cb + ct);
+    if (pos >= w1) break;
+    // the item's column tiles of this block from ct whose pairs start before w1
+    const int64_t room = tiles ? ceil_div(w1 - pos, kTileWeight) : w1 - pos;
+    const int ct_end = (int)(cb - ct < room ? cb : ct + room);
+    expand_unit<Elem>(p, slice, tiles, tiles ? item - n_g : item, c0 + ct, c0 + ct_end, s_tok, s_unscale, s_vhi,
+                      s_vlo, s_tr);
+    if (ct_end < cb) break;  // the share ends inside this item
+    ++item;
+    ct = 0;
   }
 }
 
 template <typename Elem>
 hipError_t expand_launch(const ExpandParams& p, bool groups, bool tiles, hipStream_t stream) {
   const SegLayout L = seg_layout(p.T, p.S);
-  int64_t max_out = 0;
-  for (int i = 0; i < p.n_slices; ++i) max_out = p.out_size[i] > max_out ? p.out_size[i] : max_out;
+  int64_t cols = 0;
+  for (int i = 0; i < p.n_slices; ++i) cols += ceil_div(p.out_size[i], kExpandColsPerWG);
   const int64_t cap = (groups ? L.cap_groups : 0) + (tiles ? L.cap_tiles : 0);
-  const int64_t n_ct = ceil_div(max_out, kExpandColsPerWG);
   const int grid = persistent_grid(reinterpret_cast<const void*>(&mfma_expand_kernel<Elem>), kThreads, 0,
-                                   cap * n_ct * p.n_slices);
+                                   cap * cols);
   hipLaunchKernelGGL(mfma_expand_kernel<Elem>, dim3(grid), dim3(kThreads), 0, stream, p, groups ? 1 : 0,
-                     tiles ? 1 : 0, (int)n_ct);
+                     tiles ? 1 : 0);
   return hipGetLastError();
 }
 
