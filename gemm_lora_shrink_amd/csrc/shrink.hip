@@ -111,10 +111,11 @@ __device__ inline void wait_vm(int n) {
   }
 }
 
-// Clear v columns [c0, r_max) of the unit's token rows (s_tok, -1 = none),
+// Clear v columns [c0, c1) of the unit's token rows (s_tok, -1 = none),
 // spread over the threads [first, first + count).
-__device__ inline void clear_columns(float* vb, int r_max, const int* s_tok, int cnt, int c0, int first, int count) {
-  const int w4 = (r_max - c0) / 4;  // r_max and c0 are multiples of 4
+__device__ inline void clear_columns(float* vb, int r_max, const int* s_tok, int cnt, int c0, int c1, int first,
+                                     int count) {
+  const int w4 = (c1 - c0) / 4;  // r_max, c0 and c1 are multiples of 4
   if (w4 <= 0) return;
   for (int e = threadIdx.x - first; e < cnt * w4; e += count) {
     const int row = e / w4, c = e - row * w4;
@@ -123,16 +124,18 @@ __device__ inline void clear_columns(float* vb, int r_max, const int* s_tok, int
   }
 }
 
-// One (item, part, slice) unit with RB blocks of 16 tokens and NB blocks of 16
-// ranks, over the K steps [s0, s1) of the contraction.  s_tok holds the item's
-// tokens, -1 past the count (written before a barrier); s_lds is the
+// One unit: RB blocks of 16 tokens by NB blocks of 16 ranks, over the K steps
+// [s0, s1) of the contraction.  s_tok holds the unit's tokens, -1 past the
+// count (written before a barrier); the ranks are c_lo .. c_lo + 16 NB - 1 of
+// the slot (rank r), and the unit owns v columns [c_lo, c_hi).  s_lds is the
 // workgroup's four rings.  With `partial` the unit is one of several parts of
 // the contraction: it adds its sums to v with atomics (v was cleared
-// beforehand) and leaves the other columns alone; otherwise it stores whole
-// rows.
+// beforehand) and leaves the other columns alone; otherwise it stores its
+// columns whole (zeros past the rank).
 template <typename Elem, int RB, int NB>
 __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, int s, int r, int slice, int s0,
-                                              int s1, bool partial, char* s_lds, const int* s_tok) {
+                                              int s1, bool partial, char* s_lds, const int* s_tok, int c_lo,
+                                              int c_hi) {
   using M = StepMma<Elem>;
   constexpr int kVec = Traits<Elem>::kVec;
   constexpr int kStep = 4 * kVec;  // elements per K step (64 bytes)
@@ -157,7 +160,9 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
   // 16-byte piece (l % 8) ^ (l / 8) of the batch's line of that row, and lands
   // at byte 16 l of the load's 1 KB.
   const char* xb = reinterpret_cast<const char*>(p.x);
-  const char* ab = reinterpret_cast<const char*>(p.A[slice]) + (int64_t)s * p.r_max * p.D * (int64_t)sizeof(Elem);
+  const char* ab = reinterpret_cast<const char*>(p.A[slice]) +
+                   ((int64_t)s * p.r_max + c_lo) * p.D * (int64_t)sizeof(Elem);
+  const int r_loc = min(r, c_hi) - c_lo;  // rank rows of this unit, >= 1
   const int t0 = s_tok[0];  // cnt >= 1: a valid token
   const uint32_t piece = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
   uint32_t so[NBLK][2];
@@ -172,7 +177,7 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int k = nb * 16 + row;
-      so[RB + nb][q] = (uint32_t)((int64_t)(k < r ? k : r - 1) * p.D * (int64_t)sizeof(Elem)) + piece;
+      so[RB + nb][q] = (uint32_t)((int64_t)(k < r_loc ? k : r_loc - 1) * p.D * (int64_t)sizeof(Elem)) + piece;
     }
   }
   // MFMA reads: step j of a batch gives K slot kg the piece 4 j + kg of row m
@@ -246,7 +251,7 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int k = nb * 16 + m;
-        const char* row = ab + (int64_t)(k < r ? k : r - 1) * p.D * (int64_t)sizeof(Elem);
+        const char* row = ab + (int64_t)(k < r_loc ? k : r_loc - 1) * p.D * (int64_t)sizeof(Elem);
         op[RB + nb] = ld16_or0(row + (ok ? (int64_t)d * (int64_t)sizeof(Elem) : 0), ok);
       }
 #pragma unroll
@@ -280,28 +285,54 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
       a[2] += o[2];
       a[3] += o[3];
     }
-    // lane (m, kg) holds D[token rb*16 + 4 kg + i][rank nb*16 + m]
-    const int k = nb * 16 + m;
+    // lane (m, kg) holds D[token rb*16 + 4 kg + i][rank c_lo + nb*16 + m]
+    const int k = c_lo + nb * 16 + m;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = s_tok[rb * 16 + 4 * kg + i];
       if (partial) {
         if (t >= 0 && k < r) atomicAdd(vb + (int64_t)t * p.r_max + k, a[i] * sc);
-      } else if (t >= 0 && k < p.r_max) {
+      } else if (t >= 0 && k < c_hi) {
         vb[(int64_t)t * p.r_max + k] = k < r ? a[i] * sc : 0.f;
       }
     }
   }
-  if (!partial) clear_columns(vb, p.r_max, s_tok, cnt, NB * 16, 0, kThreads);
+  if (!partial) clear_columns(vb, p.r_max, s_tok, cnt, min(c_lo + NB * 16, c_hi), c_hi, 0, kThreads);
 }
 
-// parts_t / parts_g: the contraction of every tile / group is cut into that
-// many parts (units of their own; more than 1 part means partial sums added
-// with atomics into a v cleared beforehand).  zero_units: clear the rows of
-// tokens without an adapter (not needed when v was cleared).
+// Token / rank pieces and K parts of every item of a list.
+struct Split {
+  int ts, rs, kp;  // token pieces, rank pieces, K parts
+};
+
+template <typename Elem, int RB>
+__device__ inline void contract_rb(const ShrinkParams& p, int nb, int cnt, int s, int r, int slice, int s0, int s1,
+                                   bool partial, char* s_lds, const int* s_tok, int c_lo, int c_hi) {
+  switch (nb) {
+    case 1: contract_unit<Elem, RB, 1>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
+    case 2: contract_unit<Elem, RB, 2>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
+    case 3: contract_unit<Elem, RB, 3>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
+    default: contract_unit<Elem, RB, 4>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
+  }
+}
+
+// use_tiles / use_groups: which lists of the record to work on.
+// resident: the workgroups the chip holds at once (the grid).  From the
+// record's actual item counts, items are cut into pieces while all units
+// still fit one round of the grid: each step halves the pieces of the list
+// whose units read the most rows (tokens + ranks), along the longer of the
+// two (tokens only for tiles; down to 16 tokens and 16 ranks).  Pieces write
+// disjoint v rows and columns, so they need no atomics; a token piece re-reads
+// the slot's A rows and a rank piece the item's x rows, from L2.  Splitting
+// stops short of a second round: every unit pays a fixed set-up and drain.
+// cleared: v was cleared beforehand (tiny batches).  Then lists still short
+// of about three quarters of the grid are also cut into K parts (units of
+// their own, each with at least two K steps per wave) whose partial sums are
+// added with atomics; otherwise zero units clear the rows of tokens without
+// an adapter.
 template <typename Elem>
-__global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int parts_t, int parts_g,
-                                                            int zero_units) {
+__global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int use_tiles, int use_groups,
+                                                            int resident, int cleared) {
   __shared__ __attribute__((aligned(1024))) char s_lds[kWaves * kRingBytes];
   __shared__ int s_tok[kTile];
 
@@ -309,16 +340,53 @@ __global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int
   const bool rec_ok = rec[kBuiltT] == p.T && rec[kBuiltS] == p.S;
   int na = rec_ok ? rec[kNumActive] : 0;
   na = na < 0 ? 0 : (na > p.T ? p.T : na);
-  const int64_t n_t = parts_t > 0 ? (int64_t)record_items(rec, p.T, p.S, true) * parts_t : 0;
-  const int64_t n_g = parts_g > 0 ? (int64_t)record_items(rec, p.T, p.S, false) * parts_g : 0;
-  const int64_t n_z = zero_units ? (p.T - na + kZeroRows - 1) / kZeroRows : 0;
+  const int64_t items_t = use_tiles ? record_items(rec, p.T, p.S, true) : 0;
+  const int64_t items_g = use_groups ? record_items(rec, p.T, p.S, false) : 0;
+  const int step_elems = 4 * Traits<Elem>::kVec;
+  const int n_steps = (p.D + step_elems - 1) / step_elems;
+  const int64_t ns = p.n_slices;
+  Split sp_t{1, 1, 1}, sp_g{1, 1, 1};
+  {
+    int tok_t = kTile, rk_t = p.r_max, rk_g = p.r_max;  // tokens and ranks per piece
+    int64_t u_t = items_t * ns, u_g = items_g * ns;
+    for (;;) {
+      // candidate cuts: tiles (tokens or ranks), groups (ranks)
+      const bool t_tok = tok_t > 16 && (tok_t >= rk_t || rk_t % 32 != 0);
+      const bool t_ok = u_t > 0 && (t_tok || rk_t % 32 == 0) && u_t * 2 + u_g <= resident;
+      const bool g_ok = u_g > 0 && rk_g % 32 == 0 && u_t + u_g * 2 <= resident;
+      if (t_ok && (!g_ok || tok_t + rk_t >= kGroup + rk_g)) {
+        if (t_tok) {
+          sp_t.ts *= 2;
+          tok_t /= 2;
+        } else {
+          sp_t.rs *= 2;
+          rk_t /= 2;
+        }
+        u_t *= 2;
+      } else if (g_ok) {
+        sp_g.rs *= 2;
+        rk_g /= 2;
+        u_g *= 2;
+      } else {
+        break;
+      }
+    }
+    if (cleared) {
+      const int64_t target = (int64_t)resident * 3 / 4, most = max(1, n_steps / (2 * kWaves));
+      if (u_t > 0) sp_t.kp = (int)min(most, max((int64_t)1, ceil_div(target, u_t)));
+      if (u_g > 0) sp_g.kp = (int)min(most, max((int64_t)1, ceil_div(target, u_g)));
+    }
+  }
+  const int64_t n_t = items_t * sp_t.kp * sp_t.ts * sp_t.rs;
+  const int64_t n_g = items_g * sp_g.kp * sp_g.ts * sp_g.rs;
+  const int64_t n_z = cleared ? 0 : (p.T - na + kZeroRows - 1) / kZeroRows;
   const int32_t* perm = rec + seg_layout(p.T, p.S).perm;
 
-  // Each of the three lists (tile parts, group parts, zero units; each unit
-  // once per slice, slice fastest so that the slices of one item share its x
-  // rows in one L2) is cut into 8 contiguous shares, one per XCD; the
-  // workgroups of an XCD walk the concatenation of its three shares.
-  const int64_t ns = p.n_slices;
+  // Each of the three lists (tile units, group units, zero units; each unit
+  // once per slice) is cut into 8 contiguous shares, one per XCD; the
+  // workgroups of an XCD walk the concatenation of its three shares.  Within
+  // an item the order is slice fastest, then rank piece (these units share
+  // the item's x rows in one L2), then token piece, then K part.
   const int64_t xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds, wgs = gridDim.x / kXcds;
   auto share = [&](int64_t n, int64_t& st, int64_t& ln) {
     const int64_t per = n / kXcds, rem = n % kXcds;
@@ -333,15 +401,15 @@ __global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int
 
   for (int64_t w = lb; w < ln_t + ln_g + ln_z; w += wgs) {
     const int list = w < ln_t ? 0 : (w < ln_t + ln_g ? 1 : 2);
-    const int64_t unit = list == 0 ? st_t + w : (list == 1 ? st_g + (w - ln_t) : st_z + (w - ln_t - ln_g));
-    const int64_t ip = unit / ns;  // item * parts + part (zero units: chunk)
-    const int slice = (int)(unit - ip * ns);
+    int64_t unit = list == 0 ? st_t + w : (list == 1 ? st_g + (w - ln_t) : st_z + (w - ln_t - ln_g));
+    const int slice = (int)(unit % ns);
+    unit /= ns;
     float* vb = p.v + (int64_t)slice * p.v_slice_stride;
 
     if (list == 2) {
-      // zero unit: tail entries na + 64 item .. of perm
+      // zero unit: tail entries na + 64 unit .. of perm
       const int w4 = p.r_max / 4;
-      const int64_t pos0 = na + ip * kZeroRows;
+      const int64_t pos0 = na + unit * kZeroRows;
       for (int e = tid; e < kZeroRows * w4; e += kThreads) {
         const int row = e / w4, c = e - row * w4;
         const int64_t pos = pos0 + row;
@@ -354,11 +422,16 @@ __global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int
       continue;  // no shared memory used: no barrier needed
     }
 
-    // the item's header and its tokens arrive in one memory round trip
     const bool tiles = list == 0;
-    const int parts = tiles ? parts_t : parts_g;
-    const int64_t item = ip / parts;
-    const int part = (int)(ip - item * parts);
+    const Split sp = tiles ? sp_t : sp_g;
+    const int rp = (int)(unit % sp.rs);
+    unit /= sp.rs;
+    const int tp = (int)(unit % sp.ts);
+    unit /= sp.ts;
+    const int part = (int)(unit % sp.kp);
+    const int64_t item = unit / sp.kp;
+
+    // the item's header and its tokens arrive in one memory round trip
     const int cap = tiles ? kTile : kGroup;
     const int32_t* it = item_ptr(rec, p.T, p.S, tiles, item);
     const int tv = tid < cap ? it[4 + tid] : -1;
@@ -367,74 +440,50 @@ __global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int
     if (!ok) continue;  // uniform
     if (tid < kTile) s_tok[tid] = (tid < hd.cnt && tv >= 0 && tv < p.T) ? tv : -1;
     __syncthreads();
+    // this unit's tokens and v columns
+    const int per_tok = cap / sp.ts;
+    const int tok0 = tp * per_tok;
+    const int cnt = min(per_tok, hd.cnt - tok0);
+    if (cnt <= 0) continue;  // an empty token piece; no thread reads s_tok here
+    const int per_rk = p.r_max / sp.rs;
+    const int c_lo = rp * per_rk, c_hi = c_lo + per_rk;
     const int s = __builtin_amdgcn_readfirstlane(hd.slot);
     const int r = __builtin_amdgcn_readfirstlane(slot_rank(p.ranks, s, p.r_max));
-    const int nb = (r + 15) / 16;
+    const int nb = r > c_lo ? (min(r, c_hi) - c_lo + 15) / 16 : 0;
     // this part's K steps: parts take equal runs of whole steps
-    const int step_elems = 4 * Traits<Elem>::kVec;
-    const int n_steps = (p.D + step_elems - 1) / step_elems;
-    const int per_part = (n_steps + parts - 1) / parts;
+    const int per_part = (n_steps + sp.kp - 1) / sp.kp;
     const int s0 = min(n_steps, part * per_part), s1 = min(n_steps, s0 + per_part);
-    const bool partial = parts > 1;
+    const bool partial = sp.kp > 1;
+    const int* utok = s_tok + tok0;
+    const int rbs = (cnt + 15) / 16;
     if (nb == 0) {
-      if (!partial) clear_columns(vb, p.r_max, s_tok, hd.cnt, 0, 0, kThreads);
-    } else if (hd.cnt <= 16) {
-      switch (nb) {
-        case 1: contract_unit<Elem, 1, 1>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
-        case 2: contract_unit<Elem, 1, 2>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
-        case 3: contract_unit<Elem, 1, 3>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
-        default: contract_unit<Elem, 1, 4>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
-      }
+      if (!partial) clear_columns(vb, p.r_max, utok, cnt, c_lo, c_hi, 0, kThreads);
+    } else if (rbs == 1) {
+      contract_rb<Elem, 1>(p, nb, cnt, s, r, slice, s0, s1, partial, s_lds, utok, c_lo, c_hi);
+    } else if (rbs == 2) {
+      contract_rb<Elem, 2>(p, nb, cnt, s, r, slice, s0, s1, partial, s_lds, utok, c_lo, c_hi);
     } else {
-      switch (nb) {
-        case 1: contract_unit<Elem, 4, 1>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
-        case 2: contract_unit<Elem, 4, 2>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
-        case 3: contract_unit<Elem, 4, 3>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
-        default: contract_unit<Elem, 4, 4>(p, hd.cnt, s, r, slice, s0, s1, partial, s_lds, s_tok); break;
-      }
+      contract_rb<Elem, 4>(p, nb, cnt, s, r, slice, s0, s1, partial, s_lds, utok, c_lo, c_hi);
     }
     __syncthreads();  // the next unit rewrites s_tok and the rings
   }
 }
 
-// Parts per item so that the units of a list number about `target`: at least
-// 1, and no more than leaves each wave two K steps per part.
-int parts_for(int64_t cap_units, int n_steps, int64_t target) {
-  if (cap_units <= 0) return 1;
-  int64_t parts = (target + cap_units - 1) / cap_units;
-  const int64_t most = n_steps / (2 * kWaves);
-  if (parts > most) parts = most;
-  return parts < 1 ? 1 : (int)parts;
-}
-
 template <typename Elem>
 hipError_t launch(const ShrinkParams& p, bool groups, bool tiles, hipStream_t stream) {
-  const SegLayout L = seg_layout(p.T, p.S);
   const void* kernel = reinterpret_cast<const void*>(&shrink_kernel<Elem>);
-  // The kernel is persistent.  A list whose items are too few to occupy the
-  // chip is cut into parts until its units number about three quarters of the
-  // workgroups the chip holds at once.
+  // The kernel is persistent, aiming at about three quarters of the
+  // workgroups the chip holds at once.  When even a batch of nothing but full
+  // tiles, with every piece cut, would give fewer units, items may also be
+  // cut along K: v is cleared first.
   const int resident = persistent_grid(kernel, kThreads, 0, INT64_MAX / 4);
-  const int n_steps = (int)ceil_div(p.D, 4 * Traits<Elem>::kVec);
-  const int64_t target = resident * 3 / 4;
-  const int parts_g = groups ? parts_for(L.cap_groups * p.n_slices, n_steps, target) : 0;
-  // Tiles are cut into parts only when the groups already need v cleared: the
-  // tile list's capacity counts a ragged tile for every slot, so it is mostly
-  // empty in decode-shaped batches, and a clearing launch it alone asked for
-  // would usually be wasted.
-  const int parts_t = tiles ? (parts_g > 1 || !groups ? parts_for(L.cap_tiles * p.n_slices, n_steps, target) : 1) : 0;
-  const bool cleared = parts_t > 1 || parts_g > 1;
+  const bool cleared = ceil_div(p.T, kTile) * p.n_slices * (kTile / 16) * ceil_div(p.r_max, 16) < resident * 3 / 4;
   if (cleared) {
-    // partial sums are added into v: clear it first (this also clears the
-    // rows of tokens without an adapter)
     hipError_t e = launch_fill_zero(p.v, (int64_t)p.n_slices * p.v_slice_stride, stream);
     if (e != hipSuccess) return e;
   }
-  const int64_t useful = ((tiles ? L.cap_tiles * parts_t : 0) + (groups ? L.cap_groups * parts_g : 0) +
-                          (cleared ? 0 : ceil_div(p.T, kZeroRows))) * p.n_slices;
-  const int grid = persistent_grid(kernel, kThreads, 0, useful);
-  hipLaunchKernelGGL(shrink_kernel<Elem>, dim3(grid), dim3(kThreads), 0, stream, p, parts_t, parts_g,
-                     cleared ? 0 : 1);
+  hipLaunchKernelGGL(shrink_kernel<Elem>, dim3(resident), dim3(kThreads), 0, stream, p, tiles ? 1 : 0,
+                     groups ? 1 : 0, resident, cleared ? 1 : 0);
   return hipGetLastError();
 }
 
