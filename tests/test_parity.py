@@ -64,6 +64,18 @@ def edge_problems():
         yield f"bad_idx_{dtype}", random_problem(
             rng, T=200, D=64, out_sizes=(64,), r_max=16, S=6, dtype=dtype,
             bad_idx_frac=0.2), "auto"
+    for dtype in ("f32", "f16", "bf16"):
+        # a batch large enough that the shrink cuts items into token and rank
+        # pieces rather than K parts: ragged tiles (48..200 tokens), gather
+        # groups of 1..47 tokens, ranks that are not multiples of 16
+        idx = np.concatenate([np.repeat(np.arange(6), [100, 64, 63, 200, 48, 49]),
+                              np.repeat(np.arange(6, 24), rng.integers(1, 48, 18)),
+                              np.full(600, -1)]).astype(np.int32)
+        rng.shuffle(idx)
+        p = random_problem(rng, T=idx.size, D=256, out_sizes=(128, 64), r_max=64, S=24,
+                           dtype=dtype, idx=idx, with_ranks=True)
+        p.ranks[:] = rng.integers(1, 65, 24)
+        yield f"pieces_{dtype}", p, "auto"
     for mode in ("auto", "bgmv", "sgmv"):
         # long segments (>= 48 tokens go to the segmented path in auto mode)
         idx = np.repeat(np.arange(5, dtype=np.int32), [200, 64, 63, 1, 130])
