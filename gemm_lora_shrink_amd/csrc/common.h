@@ -122,6 +122,12 @@ __device__ inline u32x4 ld16_or0(const void* p, bool ok) {
   const global_u32x4* gp = (const global_u32x4*)(ok ? p : static_cast<const void*>(g_zero16));
   return *gp;
 }
+// The same with a non-temporal hint, for data streamed once (the y rows the
+// expand reads, adds to and writes back): it is not kept in the caches.
+__device__ inline u32x4 ld16_or0_nt(const void* p, bool ok) {
+  const global_u32x4* gp = (const global_u32x4*)(ok ? p : static_cast<const void*>(g_zero16));
+  return __builtin_nontemporal_load(gp);
+}
 __device__ inline f32x4 ldf4_or0(const float* p, bool ok) {
   const global_f32x4* gp =
       (const global_f32x4*)(ok ? static_cast<const void*>(p) : static_cast<const void*>(g_zero16));

@@ -121,7 +121,7 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
       for (int h = 0; h < 2; ++h) {
         const int t = sb < n_sub ? s_tok[sb * 16 + h * 8 + yr] : -1;
         const bool ok = ycol_ok && t >= 0;
-        dst[sb][h] = ld16_or0(ok ? ybase + jw + (int64_t)t * p.ldy : yzero, ok);
+        dst[sb][h] = ld16_or0_nt(ok ? ybase + jw + (int64_t)t * p.ldy : yzero, ok);
       }
   };
   // A operand: this wave's 64 B rows of column tile `ct` (4 blocks x 16), both
@@ -244,7 +244,9 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
             if constexpr (Tr::kDtype == LORA_BF16) o[q] = pack2_bf16(y0, y1);
             else o[q] = pack2_f16(y0, y1);
           }
-          *reinterpret_cast<u32x4*>(ybase + jw + (int64_t)t * p.ldy) = o;
+          // y is streamed once: non-temporal, so that it does not sit dirty in
+          // L2 for the kernels that follow
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(ybase + jw + (int64_t)t * p.ldy));
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -387,7 +389,7 @@ __device__ inline void expand_group_direct(const ExpandParams& p, int tok_n, int
           if constexpr (Tr::kDtype == LORA_BF16) o[q] = pack2_bf16(y0, y1);
           else o[q] = pack2_f16(y0, y1);
         }
-        *reinterpret_cast<u32x4*>(ybase + jw + (int64_t)t * p.ldy) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(ybase + jw + (int64_t)t * p.ldy));
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
