@@ -288,8 +288,8 @@ __device__ inline void expand_group_direct(const ExpandParams& p, int tok_n, int
   auto load_tile = [&](int ct, u32x4 (&yd)[2], u32x4 (&bd)[4][2]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
     const bool ycol_ok = ct < ct_end && jw + yc < out;  // out is a multiple of 8
-    yd[0] = ld16_or0(ycol_ok && ytok0 >= 0 ? ybase + jw + (int64_t)ytok0 * p.ldy : yzero, ycol_ok && ytok0 >= 0);
-    yd[1] = ld16_or0(ycol_ok && ytok1 >= 0 ? ybase + jw + (int64_t)ytok1 * p.ldy : yzero, ycol_ok && ytok1 >= 0);
+    yd[0] = ld16_or0_nt(ycol_ok && ytok0 >= 0 ? ybase + jw + (int64_t)ytok0 * p.ldy : yzero, ycol_ok && ytok0 >= 0);
+    yd[1] = ld16_or0_nt(ycol_ok && ytok1 >= 0 ? ybase + jw + (int64_t)ytok1 * p.ldy : yzero, ycol_ok && ytok1 >= 0);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int row = jw + cb * 16 + n;

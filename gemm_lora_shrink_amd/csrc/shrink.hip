@@ -89,6 +89,19 @@ __device__ inline void load_to_lds(const char* base, uint32_t voff, uint32_t lds
       : "s"(lds), "v"(voff), "s"(base)
       : "memory");
 }
+// The same with a non-temporal hint, for rows read once.
+__device__ inline void load_to_lds_nt(const char* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory");
+}
 
 // Wait until at most n (a multiple of `unit`, at most 7 units and at most 63,
 // the counter's range) of this wave's vector memory operations are outstanding.
@@ -131,8 +144,10 @@ __device__ inline void clear_columns(float* vb, int r_max, const int* s_tok, int
 // workgroup's four rings.  With `partial` the unit is one of several parts of
 // the contraction: it adds its sums to v with atomics (v was cleared
 // beforehand) and leaves the other columns alone; otherwise it stores its
-// columns whole (zeros past the rank).
-template <typename Elem, int RB, int NB>
+// columns whole (zeros past the rank).  XONCE: no other unit reads this
+// unit's x rows (one slice, no rank pieces), so they are loaded with a
+// non-temporal hint and do not displace reused data from the caches.
+template <typename Elem, int RB, int NB, bool XONCE>
 __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, int s, int r, int slice, int s0,
                                               int s1, bool partial, char* s_lds, const int* s_tok, int c_lo,
                                               int c_hi) {
@@ -204,7 +219,8 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
     for (int bk = 0; bk < NBLK; ++bk)
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        load_to_lds(bk < RB ? xb : ab, so[bk][q] + boff, dst + (uint32_t)(bk * kBlockBytes + q * 1024));
+        if (XONCE && bk < RB) load_to_lds_nt(xb, so[bk][q] + boff, dst + (uint32_t)(bk * kBlockBytes + q * 1024));
+        else load_to_lds(bk < RB ? xb : ab, so[bk][q] + boff, dst + (uint32_t)(bk * kBlockBytes + q * 1024));
   };
   int issued = 0;
   for (; issued < my_n && issued < DEPTH; ++issued) issue(issued);
@@ -305,15 +321,23 @@ struct Split {
   int ts, rs, kp;  // token pieces, rank pieces, K parts
 };
 
-template <typename Elem, int RB>
+template <typename Elem, int RB, bool XONCE>
 __device__ inline void contract_rb(const ShrinkParams& p, int nb, int cnt, int s, int r, int slice, int s0, int s1,
                                    bool partial, char* s_lds, const int* s_tok, int c_lo, int c_hi) {
   switch (nb) {
-    case 1: contract_unit<Elem, RB, 1>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
-    case 2: contract_unit<Elem, RB, 2>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
-    case 3: contract_unit<Elem, RB, 3>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
-    default: contract_unit<Elem, RB, 4>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
+    case 1: contract_unit<Elem, RB, 1, XONCE>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
+    case 2: contract_unit<Elem, RB, 2, XONCE>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
+    case 3: contract_unit<Elem, RB, 3, XONCE>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
+    default: contract_unit<Elem, RB, 4, XONCE>(p, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi); break;
   }
+}
+
+template <typename Elem, bool XONCE>
+__device__ inline void contract_any(const ShrinkParams& p, int rbs, int nb, int cnt, int s, int r, int slice, int s0,
+                                    int s1, bool partial, char* s_lds, const int* s_tok, int c_lo, int c_hi) {
+  if (rbs == 1) contract_rb<Elem, 1, XONCE>(p, nb, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi);
+  else if (rbs == 2) contract_rb<Elem, 2, XONCE>(p, nb, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi);
+  else contract_rb<Elem, 4, XONCE>(p, nb, cnt, s, r, slice, s0, s1, partial, s_lds, s_tok, c_lo, c_hi);
 }
 
 // use_tiles / use_groups: which lists of the record to work on.
@@ -455,15 +479,14 @@ __global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int
     const int s0 = min(n_steps, part * per_part), s1 = min(n_steps, s0 + per_part);
     const bool partial = sp.kp > 1;
     const int* utok = s_tok + tok0;
+    const bool x_once = ns == 1 && sp.rs == 1;
     const int rbs = (cnt + 15) / 16;
     if (nb == 0) {
       if (!partial) clear_columns(vb, p.r_max, utok, cnt, c_lo, c_hi, 0, kThreads);
-    } else if (rbs == 1) {
-      contract_rb<Elem, 1>(p, nb, cnt, s, r, slice, s0, s1, partial, s_lds, utok, c_lo, c_hi);
-    } else if (rbs == 2) {
-      contract_rb<Elem, 2>(p, nb, cnt, s, r, slice, s0, s1, partial, s_lds, utok, c_lo, c_hi);
+    } else if (x_once) {
+      contract_any<Elem, true>(p, rbs, nb, cnt, s, r, slice, s0, s1, partial, s_lds, utok, c_lo, c_hi);
     } else {
-      contract_rb<Elem, 4>(p, nb, cnt, s, r, slice, s0, s1, partial, s_lds, utok, c_lo, c_hi);
+      contract_any<Elem, false>(p, rbs, nb, cnt, s, r, slice, s0, s1, partial, s_lds, utok, c_lo, c_hi);
     }
     __syncthreads();  // the next unit rewrites s_tok and the rings
   }
