@@ -60,15 +60,39 @@ __device__ inline uint64_t wave_peers(int key, bool valid, int nbits) {
   return valid ? peers : 0;
 }
 
-// Inclusive scan of one int across the wave.
+// Cross-lane moves on the DPP network (no LDS round trip): lane i of a row of
+// 16 takes lane i - n of its row (0 past the row's start); a row broadcast
+// hands lane 15 (31) to the rows selected by the mask (rows 1 and 3 for lane
+// 15, rows 2 and 3 for lane 31), the other rows receiving 0.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline int dpp_or0(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, true);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive scan of one int across the wave: within rows of 16 by shifts of
+// 1, 2, 4, 8, then across rows by the two broadcasts.
 __device__ inline int wave_inclusive_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int u = __shfl_up(v, off, 64);
-    if (lane >= off) v += u;
-  }
+  v += dpp_or0<kRowShr1>(v);
+  v += dpp_or0<kRowShr2>(v);
+  v += dpp_or0<kRowShr4>(v);
+  v += dpp_or0<kRowShr8>(v);
+  v += dpp_or0<kRowBcast15, 0xa>(v);
+  v += dpp_or0<kRowBcast31, 0xc>(v);
   return v;
+}
+
+// Maximum of one non-negative int over the wave (the same pattern with max;
+// 0 is the identity), returned to every lane.
+__device__ inline int wave_max_nonneg(int v) {
+  v = max(v, dpp_or0<kRowShr1>(v));
+  v = max(v, dpp_or0<kRowShr2>(v));
+  v = max(v, dpp_or0<kRowShr4>(v));
+  v = max(v, dpp_or0<kRowShr8>(v));
+  v = max(v, dpp_or0<kRowBcast15, 0xa>(v));
+  v = max(v, dpp_or0<kRowBcast31, 0xc>(v));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Block-wide exclusive scan of four ints per thread (thread order), returning
@@ -164,6 +188,14 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   // 1. per-(wave, key) counts
   int bad = 0;
   uint64_t peers_reg[kRegChunks];
+  // A chunk whose valid lanes all hold one key (a prefill segment) adds to a
+  // pending run kept in registers, flushed when the key changes, so that long
+  // segments do not chain one LDS read-modify-write per chunk.
+  int run_key = -1, run_cnt = 0;
+  auto flush_run = [&]() {
+    if (run_cnt > 0 && lane == 0) s_tab[wave][run_key] += run_cnt;
+    run_cnt = 0;
+  };
   auto count_chunk = [&](int t, int& k) -> uint64_t {
     const bool valid = t < T;
     if (valid && !(k >= 0 && k < S)) {
@@ -171,7 +203,17 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
       k = S;
     }
     const uint64_t peers = wave_peers(k, valid, nbits);
-    if (valid && (peers & lt_mask) == 0) s_tab[wave][k] += __popcll(peers);  // one lane per key
+    const uint64_t all = __ballot(valid);
+    if (all != 0 && __ballot(valid && peers == all) == all) {  // uniform: one key in the whole chunk
+      const int key0 = __builtin_amdgcn_readfirstlane(k);
+      if (key0 != run_key) {
+        flush_run();
+        run_key = key0;
+      }
+      run_cnt += __popcll(all);
+    } else if (valid && (peers & lt_mask) == 0) {
+      s_tab[wave][k] += __popcll(peers);  // one lane per key
+    }
     return peers;
   };
 #pragma unroll
@@ -184,6 +226,7 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
     int k = t < T ? idx[t] : -1;
     count_chunk(t, k);
   }
+  flush_run();
   if (bad) s_bad = 1;  // benign: every writer stores 1
   lds_barrier();
 
@@ -198,7 +241,10 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
     const bool to_tiles = (mode == LORA_MODE_SGMV) || (mode == LORA_MODE_AUTO && n_slot >= kSgmvMinTokens);
     if (to_tiles) nt = (int)ceil_div(n_slot, kTile);
     else ng = (int)ceil_div(n_slot, kGroup);
-    atomicMax(&s_maxlen, n_slot);
+  }
+  if (wave * 64 < S) {  // uniform: one LDS atomic per wave, not one per slot
+    const int wmax = wave_max_nonneg(n_slot);
+    if (lane == 0) atomicMax(&s_maxlen, wmax);
   }
   int4 sc = make_int4(n_slot, n_slot > 0 ? 1 : 0, ng, nt);
   int4 tot;
@@ -208,11 +254,13 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   // token; with S = 1024 thread 0 also takes it)
   for (int k = tid; k <= S; k += kThreads) {
     int run = k < S ? sc.x : num_active;
+    int c[kWaves];  // every count is read before any start is written
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) c[w] = s_tab[w][k];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const int c = s_tab[w][k];
       s_tab[w][k] = run;
-      run += c;
+      run += c[w];
     }
   }
   if (tid < S) {
