@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
     ap.add_argument("--eager", action="store_true", help="time host launches instead of graph replay")
+    ap.add_argument("--path", default="fused", choices=["fused", "split"],
+                    help="fused: each layer with a timed expand is one shrink_expand call (one "
+                         "launch for 16-bit batches up to lora_fused_max_tokens(), else two); "
+                         "split: a shrink call then an expand call")
     ap.add_argument("--no-calls", action="store_true",
                     help="skip the per-call timing (counter runs: kernels then run in step order only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -205,6 +209,7 @@ def main():
             c = {k: (v.clone() if torch.is_tensor(v) else [t.clone() for t in v] if isinstance(v, list) else v)
                  for k, v in d.items()}
             c["v"] = torch.empty((p.n_slices, T, p.r_max), dtype=torch.float32, device=dev)
+            c["ws"] = glsa.alloc_workspace(T, S, p.n_slices, p.r_max, dev)
             layers.append(c)
         seg = glsa.alloc_segments(T, S, dev)
         sets.append(dict(idx=layers[0]["idx"], seg=seg, layers=layers))
@@ -223,9 +228,20 @@ def main():
         glsa.expand(d["v"], d["B"], d["y"], st["seg"], p.out_offsets, ranks=d["ranks"],
                     active=active)
 
+    def do_fused(st, li):
+        d, p = st["layers"][li], problems[li]
+        glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], st["seg"], p.out_offsets,
+                           workspace=d["ws"], scale=d["scale"], ranks=d["ranks"], v=d["v"],
+                           active=active)
+
+    fused = args.path == "fused"
+
     def step(st):
         do_segments(st)
         for li, p in enumerate(problems):
+            if fused and p.timed_expand:
+                do_fused(st, li)
+                continue
             do_shrink(st, li)
             if p.timed_expand:
                 do_expand(st, li)
@@ -313,6 +329,12 @@ def main():
                              flops=0)
     if active:
         for li, p in enumerate(problems):
+            if fused and p.timed_expand:
+                calls[f"{p.name}.shrink_expand"] = dict(
+                    us=call_time_us(lambda st, li=li: do_fused(st, li)),
+                    bytes=alg[li]["shrink_bytes"] + alg[li]["expand_bytes"],
+                    flops=alg[li]["shrink_flops"] + alg[li]["expand_flops"])
+                continue
             calls[f"{p.name}.shrink"] = dict(us=call_time_us(lambda st, li=li: do_shrink(st, li)),
                                              bytes=alg[li]["shrink_bytes"], flops=alg[li]["shrink_flops"])
             if p.timed_expand:
@@ -346,7 +368,7 @@ def main():
                     layers=[dict(name=p.name, D=p.D, out=list(p.out_sizes),
                                  timed_expand=p.timed_expand) for p in problems],
                     n_active=alg[0]["n_active"], n_distinct_slots=alg[0]["n_distinct"],
-                    mode=args.mode, timing=timed_mode, input_sets=n_sets,
+                    mode=args.mode, path=args.path, timing=timed_mode, input_sets=n_sets,
                     accumulate="fp32"),
         step_gbs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         step_tflops=round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),

@@ -11,6 +11,9 @@ Entry points (same names as the C ABI):
     shrink(x, A, seg, ...)               -> v  [n_slices, T, r_max] fp32
     expand(v, B, y, seg, out_offsets, ...) (y updated in place)
     apply(x, A, B, y, seg, out_offsets, ...) = shrink then expand
+    shrink_expand(x, A, B, y, seg, out_offsets, workspace=..., ...)
+                                         the same in one call (one launch for 16-bit data)
+    alloc_workspace(T, S, n_slices, r_max, device) -> zeroed workspace for it
 """
 
 import ctypes
@@ -70,6 +73,13 @@ def _load():
     lib.lora_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, vp, vp, vp, i32, i32, vp, vp,
                                 i32, vp, i64, vp]
     lib.lora_expand.restype = ctypes.c_int
+    lib.lora_fused_max_tokens.argtypes = []
+    lib.lora_fused_max_tokens.restype = i32
+    lib.lora_shrink_expand_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.lora_shrink_expand_workspace_bytes.restype = sz
+    lib.lora_shrink_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp, i32,
+                                       i32, vp, vp, vp, i32, vp, vp, i64, vp, sz, vp]
+    lib.lora_shrink_expand.restype = ctypes.c_int
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_last_error.argtypes = []
@@ -223,3 +233,66 @@ def apply(x, A, B, y, seg, out_offsets, *, scale=None, ranks=None, v=None, activ
     v = shrink(x, A, seg, scale=scale, ranks=ranks, v=v, active=active, stream=stream)
     expand(v, B, y, seg, out_offsets, ranks=ranks, active=active, stream=stream)
     return v, y
+
+
+def fused_max_tokens():
+    return int(_load().lora_fused_max_tokens())
+
+
+def workspace_bytes(T, S, n_slices, r_max):
+    return int(_load().lora_shrink_expand_workspace_bytes(T, S, n_slices, r_max))
+
+
+def alloc_workspace(T, S, n_slices, r_max, device):
+    """A zeroed workspace for shrink_expand (uint8 tensor, 256-byte aligned)."""
+    n = workspace_bytes(T, S, n_slices, r_max)
+    if n == 0:
+        raise LoraError(LORA_ERR_INVALID_ARG, f"bad sizes T={T} S={S} n_slices={n_slices} r_max={r_max}")
+    ws = torch.zeros(n, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise LoraError(LORA_ERR_INVALID_ARG, "allocator returned a workspace not aligned to 256 bytes")
+    return ws
+
+
+def workspace_errors(ws):
+    """Device-side waits that gave up in calls on this workspace (0 normally)."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=None, v=None,
+                  active=True, stream=None):
+    """Shrink then expand in one call; y updated in place.  Returns y.
+
+    v (optional, [n_slices, T, r_max] float32) receives the intermediate.
+    workspace: from alloc_workspace (zeroed once; every call leaves it reusable).
+    """
+    A, B = list(A), list(B)
+    if not A or len(A) > MAX_SLICES or len(B) != len(A):
+        raise LoraError(LORA_ERR_INVALID_ARG, f"need 1..{MAX_SLICES} slices, as many B as A")
+    S, r_max, D = A[0].shape
+    T, _, ldx = _rows(x, "x")
+    _, _, ldy = _rows(y, "y")
+    for a in A:
+        if a.shape != (S, r_max, D) or not a.is_contiguous() or a.dtype != x.dtype:
+            raise LoraError(LORA_ERR_INVALID_ARG, "A slices must share shape, dtype and be contiguous")
+    for b in B:
+        if b.shape[0] != S or b.shape[2] != r_max or not b.is_contiguous() or b.dtype != y.dtype:
+            raise LoraError(LORA_ERR_INVALID_ARG, "B slices must share S, r_max, dtype and be contiguous")
+    if y.dtype != x.dtype:
+        raise LoraError(LORA_ERR_INVALID_ARG, "x and y must share one dtype")
+    if v is not None and (v.dtype != torch.float32 or not v.is_contiguous()
+                          or v.shape != (len(A), T, r_max)):
+        raise LoraError(LORA_ERR_INVALID_ARG, "v must be contiguous float32 [n_slices, T, r_max]")
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise LoraError(LORA_ERR_INVALID_ARG, "workspace must be a contiguous uint8 tensor")
+    n = len(A)
+    a_ptrs = (ctypes.c_void_p * n)(*[a.data_ptr() for a in A])
+    b_ptrs = (ctypes.c_void_p * n)(*[b.data_ptr() for b in B])
+    sizes = (ctypes.c_int64 * n)(*[b.shape[1] for b in B])
+    offs = (ctypes.c_int64 * n)(*[int(o) for o in out_offsets])
+    st = _load().lora_shrink_expand(_dtype_code(x), _ptr(x), ldx, T, D, n, a_ptrs, b_ptrs, sizes, offs,
+                                    S, r_max, _ptr(ranks), _ptr(scale), _ptr(seg), 1 if active else 0,
+                                    _ptr(v), _ptr(y), ldy, _ptr(workspace), workspace.numel(),
+                                    _stream(stream, x.device))
+    _check(st)
+    return y

@@ -129,6 +129,8 @@ LORA_EXPORT const char* lora_last_error(void) { return g_err; }
 
 LORA_EXPORT int32_t lora_sgmv_min_tokens(void) { return kSgmvMinTokens; }
 
+LORA_EXPORT int32_t lora_fused_max_tokens(void) { return kFusedMaxTokens; }
+
 LORA_EXPORT size_t lora_segments_bytes(int32_t T, int32_t S) {
   if (T < 0 || S < 1 || S > LORA_MAX_SLOTS) return 0;
   const SegLayout L = seg_layout(T, S);
@@ -170,11 +172,14 @@ LORA_EXPORT lora_status lora_build_segments(const int32_t* idx, int32_t T, int32
   return LORA_OK;
 }
 
-LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D,
-                                    int32_t n_slices, const void* const* A, int32_t S, int32_t r_max,
-                                    const int32_t* ranks, const float* scale, const void* seg,
-                                    int32_t active_hint, float* v, hipStream_t stream) {
-  clear_error();
+namespace lora {
+namespace {
+
+// Host checks of the shrink arguments; fills p (everything but the v pointer
+// check happens here; v is checked by the caller).
+lora_status prep_shrink(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D, int32_t n_slices,
+                        const void* const* A, int32_t S, int32_t r_max, const int32_t* ranks, const float* scale,
+                        const void* seg, float* v, ShrinkParams& p) {
   lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
   if (st != LORA_OK) return st;
   const int vec = vec_of(dt);
@@ -184,7 +189,7 @@ LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, i
   if (D % vec || ldx % vec)
     return fail(LORA_ERR_UNSUPPORTED, "D and ldx must be multiples of %d elements for this dtype", vec);
   if (!x || !v) return fail(LORA_ERR_INVALID_ARG, "x or v is null");
-  // the shrink kernel addresses x and one slot's A rows with 32-bit byte offsets
+  // the shrink kernels address x and one slot's A rows with 32-bit byte offsets
   const uint64_t esize = dt == LORA_F32 ? 4 : 2;
   if (((uint64_t)(T - 1) * (uint64_t)ldx + (uint64_t)D) * esize > 0xFFFFFFFFull)
     return fail(LORA_ERR_UNSUPPORTED, "x spans more than 4 GiB");
@@ -192,14 +197,12 @@ LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, i
     return fail(LORA_ERR_UNSUPPORTED, "one slot's A rows span more than 4 GiB");
   if (!aligned16(x) || !aligned16(v)) return fail(LORA_ERR_UNSUPPORTED, "x and v must be 16-byte aligned");
   if (!A) return fail(LORA_ERR_INVALID_ARG, "A pointer array is null");
-  ShrinkParams p = {};
+  p = ShrinkParams{};
   for (int i = 0; i < n_slices; ++i) {
     if (!A[i]) return fail(LORA_ERR_INVALID_ARG, "A[%d] is null", i);
     if (!aligned16(A[i])) return fail(LORA_ERR_UNSUPPORTED, "A[%d] must be 16-byte aligned", i);
     p.A[i] = A[i];
   }
-  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
-
   p.x = x;
   p.ldx = ldx;
   p.ranks = ranks;
@@ -212,20 +215,14 @@ LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, i
   p.r_max = r_max;
   p.n_slices = n_slices;
   p.T = T;
-
-  // One launch shrinks every work item and leaves v fully written (preceded by
-  // a clearing launch when items are cut into parts summed with atomics).
-  const hipError_t e = launch_shrink(dt, p, /*groups=*/true, /*tiles=*/true, stream);
-  if (e != hipSuccess) return hip_fail(e, "shrink launch");
   return LORA_OK;
 }
 
-LORA_EXPORT lora_status lora_expand(lora_dtype dt, const float* v, int64_t v_slice_stride, int32_t T,
-                                    int32_t n_slices, const void* const* B, const int64_t* out_sizes,
-                                    const int64_t* out_offsets, int32_t S, int32_t r_max, const int32_t* ranks,
-                                    const void* seg, int32_t active_hint, void* y, int64_t ldy,
-                                    hipStream_t stream) {
-  clear_error();
+// Host checks of the expand arguments; fills p.
+lora_status prep_expand(lora_dtype dt, const float* v, int64_t v_slice_stride, int32_t T, int32_t n_slices,
+                        const void* const* B, const int64_t* out_sizes, const int64_t* out_offsets, int32_t S,
+                        int32_t r_max, const int32_t* ranks, const void* seg, void* y, int64_t ldy,
+                        ExpandParams& p) {
   lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
   if (st != LORA_OK) return st;
   const int vec = vec_of(dt);
@@ -238,7 +235,7 @@ LORA_EXPORT lora_status lora_expand(lora_dtype dt, const float* v, int64_t v_sli
   if (v_slice_stride != 0 && v_slice_stride < (int64_t)T * r_max)
     return fail(LORA_ERR_INVALID_ARG, "v_slice_stride is smaller than T * r_max");
   if (ldy < 1 || ldy % vec) return fail(LORA_ERR_UNSUPPORTED, "ldy must be a positive multiple of %d", vec);
-  ExpandParams p = {};
+  p = ExpandParams{};
   std::vector<std::pair<int64_t, int64_t>> cols;
   for (int i = 0; i < n_slices; ++i) {
     if (!B[i]) return fail(LORA_ERR_INVALID_ARG, "B[%d] is null", i);
@@ -258,8 +255,6 @@ LORA_EXPORT lora_status lora_expand(lora_dtype dt, const float* v, int64_t v_sli
   std::sort(cols.begin(), cols.end());
   for (size_t i = 1; i < cols.size(); ++i)
     if (cols[i].first < cols[i - 1].second) return fail(LORA_ERR_INVALID_ARG, "output slices overlap");
-  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
-
   p.v = v;
   p.v_slice_stride = v_slice_stride;
   p.ranks = ranks;
@@ -270,7 +265,11 @@ LORA_EXPORT lora_status lora_expand(lora_dtype dt, const float* v, int64_t v_sli
   p.r_max = r_max;
   p.n_slices = n_slices;
   p.T = T;
+  return LORA_OK;
+}
 
+// The expand launches of the record's items.
+hipError_t run_expand(lora_dtype dt, const ExpandParams& p, hipStream_t stream) {
   hipError_t e;
   if (dt == LORA_F32) {
     e = launch_bgmv_expand(dt, p, /*tiles=*/false, stream);
@@ -281,6 +280,88 @@ LORA_EXPORT lora_status lora_expand(lora_dtype dt, const float* v, int64_t v_sli
   } else {
     e = launch_mfma_expand(dt, p, /*groups=*/true, /*tiles=*/true, stream);
   }
+  return e;
+}
+
+}  // namespace
+}  // namespace lora
+
+LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D,
+                                    int32_t n_slices, const void* const* A, int32_t S, int32_t r_max,
+                                    const int32_t* ranks, const float* scale, const void* seg,
+                                    int32_t active_hint, float* v, hipStream_t stream) {
+  clear_error();
+  ShrinkParams p;
+  const lora_status st = prep_shrink(dt, x, ldx, T, D, n_slices, A, S, r_max, ranks, scale, seg, v, p);
+  if (st != LORA_OK || T == 0) return st;
+  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
+  // One launch shrinks every work item and leaves v fully written (preceded by
+  // a clearing launch when items are cut into parts summed with atomics).
+  const hipError_t e = launch_shrink(dt, p, /*groups=*/true, /*tiles=*/true, stream);
+  if (e != hipSuccess) return hip_fail(e, "shrink launch");
+  return LORA_OK;
+}
+
+LORA_EXPORT lora_status lora_expand(lora_dtype dt, const float* v, int64_t v_slice_stride, int32_t T,
+                                    int32_t n_slices, const void* const* B, const int64_t* out_sizes,
+                                    const int64_t* out_offsets, int32_t S, int32_t r_max, const int32_t* ranks,
+                                    const void* seg, int32_t active_hint, void* y, int64_t ldy,
+                                    hipStream_t stream) {
+  clear_error();
+  ExpandParams p;
+  const lora_status st =
+      prep_expand(dt, v, v_slice_stride, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks, seg, y, ldy, p);
+  if (st != LORA_OK || T == 0) return st;
+  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
+  const hipError_t e = run_expand(dt, p, stream);
   if (e != hipSuccess) return hip_fail(e, "expand launch");
+  return LORA_OK;
+}
+
+LORA_EXPORT size_t lora_shrink_expand_workspace_bytes(int32_t T, int32_t S, int32_t n_slices, int32_t r_max) {
+  if (T < 0 || S < 1 || S > LORA_MAX_SLOTS || n_slices < 1 || n_slices > LORA_MAX_SLICES || r_max < 1 ||
+      r_max > LORA_MAX_RANK)
+    return 0;
+  return (size_t)fused_need_bytes(T, S, n_slices, r_max);
+}
+
+LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D,
+                                           int32_t n_slices, const void* const* A, const void* const* B,
+                                           const int64_t* out_sizes, const int64_t* out_offsets, int32_t S,
+                                           int32_t r_max, const int32_t* ranks, const float* scale, const void* seg,
+                                           int32_t active_hint, float* v, void* y, int64_t ldy, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
+  if (st != LORA_OK) return st;
+  if (!workspace) return fail(LORA_ERR_INVALID_ARG, "workspace is null");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(LORA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int64_t need = fused_need_bytes(T, S, n_slices, r_max);
+  if ((int64_t)workspace_bytes < need)
+    return fail(LORA_ERR_INVALID_ARG, "workspace has %zu bytes, the call needs %lld", workspace_bytes,
+                (long long)need);
+  char* ws = static_cast<char*>(workspace);
+  // without a caller v, the two-launch form keeps v in the workspace's data
+  // region (never in the header or the counters)
+  float* v_eff = v ? v : reinterpret_cast<float*>(ws + fused_layout((int64_t)workspace_bytes).part);
+  ShrinkParams sp;
+  st = prep_shrink(dt, x, ldx, T, D, n_slices, A, S, r_max, ranks, scale, seg, v_eff, sp);
+  if (st != LORA_OK) return st;
+  ExpandParams ep;
+  st = prep_expand(dt, v_eff, (int64_t)T * r_max, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks, seg, y,
+                   ldy, ep);
+  if (st != LORA_OK || T == 0) return st;
+  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
+  hipError_t e;
+  if (dt != LORA_F32 && T <= kFusedMaxTokens) {
+    e = launch_fused(dt, sp, ep, ws, (int64_t)workspace_bytes, v, stream);
+  } else {
+    // larger batches stream enough bytes per launch that the launch and the
+    // round trips no longer dominate: the shrink launch then the expand launch
+    e = launch_shrink(dt, sp, /*groups=*/true, /*tiles=*/true, stream);
+    if (e == hipSuccess) e = run_expand(dt, ep, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "shrink-expand launch");
   return LORA_OK;
 }

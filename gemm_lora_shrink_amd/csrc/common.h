@@ -16,6 +16,7 @@ constexpr int kInfoWords = 16;
 constexpr int kGroup = 16;  // tokens per gather (BGMV) work item
 constexpr int kTile = 64;   // tokens per segmented (SGMV) work item
 constexpr int kSgmvMinTokens = 48;  // AUTO: slots with this many tokens go to SGMV
+constexpr int kFusedMaxTokens = 2048;  // lora_shrink_expand runs as one launch up to this T
 
 enum InfoWord {
   kNumActive = 0,
@@ -313,5 +314,20 @@ hipError_t launch_bgmv_expand(lora_dtype dt, const ExpandParams& p, bool tiles, 
 // Matrix-core expand over the gather groups and/or the segmented tiles, in one
 // launch (16-bit types only).
 hipError_t launch_mfma_expand(lora_dtype dt, const ExpandParams& p, bool groups, bool tiles, hipStream_t stream);
+
+// Workspace of the fused shrink-expand call.  The layout depends only on the
+// workspace's size: word 0 counts waits that gave up, the per-chunk counters
+// fill [counters, counters + counter_bytes), the producer slabs (or v, when
+// the call runs as two launches) start at `part`.
+struct FusedLayout {
+  int64_t counters, counter_bytes, part;
+};
+FusedLayout fused_layout(int64_t bytes);
+// Smallest workspace for a call of this shape.
+int64_t fused_need_bytes(int64_t T, int64_t S, int64_t n_slices, int64_t r_max);
+// Shrink and expand of the record's items in one launch (16-bit types only);
+// v_out (nullable) receives v in full.
+hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, char* ws,
+                        int64_t ws_bytes, float* v_out, hipStream_t stream);
 
 }  // namespace lora

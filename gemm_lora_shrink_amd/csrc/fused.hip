@@ -1,0 +1,326 @@
+// Fused shrink + expand of one LoRA layer in a single launch, for 16-bit data:
+//   v[i][t][k]        = scale[s] * sum_d A_i[s][k][d] * x[t][d]
+//   y[t][off_i + j]  += sum_k B_i[s][j][k] * v[i][t][k]
+// (the shrink and expand of "Add multi-LoRA support"; the intermediate is fp32
+// throughout, as that page's Limitations ask).
+//
+// Decode-shaped batches move a few MB per layer, and separate shrink and
+// expand launches spend most of their time in launch, set-up and the chain of
+// dependent memory round trips.  Here the work is cut into 16-token chunks (a
+// gather group, or a quarter of a segmented tile) and one launch runs
+//   - producer units (chunk, K part, slice): the chunk's [16 x D] by [D x r]
+//     contraction over one range of K, on the matrix cores (shrink_unit.h),
+//     stored raw into the part's slab of the caller's workspace;
+//   - consumer units (chunk, slice, run of 256-column tiles): the expand of the
+//     chunk (expand_unit.h), whose fp32 v is the sum of the chunk's slabs, in
+//     part order, times the slot's scale.
+// A producer stores its slab with device-coherent (agent scope) stores, which
+// write through the XCD's L2, waits until they are complete, then increments
+// the chunk's counter (a device-coherent atomic).  A consumer requests its
+// first y and B rows, polls the counter with device-coherent loads until it
+// shows every part, then reads the slabs with ordinary cached loads: no cache
+// on the chip can hold a stale copy of a slab line, since every L2 and L1 is
+// invalidated when a kernel starts, and in this launch nothing reads a slab
+// line before its chunk's counter is complete (slabs are whole 128-byte
+// lines, written by one producer unit).  The other consumers of the chunk then
+// hit in L2.  (Release and acquire fences at agent scope would instead write
+// back or invalidate a whole L2 per wave, which costs far more than the
+// layer.)  Every workgroup
+// runs all of its producer units before any consumer unit, and the grid is
+// no larger than what the chip holds at once, so every producer runs while
+// consumers wait; a wait still gives up after a bounded number of polls (and
+// counts itself in the workspace's error word), so every wave exits.
+//   The counters start at zero.  Consumers add their column tiles to the same
+// counter, and the one that brings it to its final value (every part and
+// every column tile of the chunk) sets it back to zero, so the next call
+// starts from zero again without a clearing pass.  The workspace layout
+// depends only on its size (counters in its first quarter, after a 256-byte
+// header), so calls of any shape on one workspace use the same counter region
+// and never write their slabs over another call's counters.
+#include "common.h"
+#include "expand_unit.h"
+#include "shrink_unit.h"
+
+namespace lora {
+
+namespace {
+
+constexpr int kFThreads = kUnitThreads;
+constexpr int kFRing = 16384;        // per-wave LDS ring: 64 KB per workgroup, two workgroups per CU
+constexpr int kMaxParts = 8;         // K parts per chunk
+constexpr int kFusedUnits = 1024;    // at most this many producer slabs when chunks are cut into K parts
+constexpr int kSpinLimit = 1 << 20;  // polls (about a microsecond each) before a wait gives up
+constexpr int kZeroRowsF = 64;       // tail entries per zero unit
+constexpr int kCounterStride = 32;   // int32 words between counters: one 128-byte line each
+
+struct FusedParams {
+  ShrinkParams sp;
+  ExpandParams ep;
+  float* part;        // producer slabs, [slab][16][r_max] fp32
+  int32_t* counters;  // [n_slices * chunk_cap]
+  int32_t* err;       // waits that gave up
+  float* v_out;       // nullable: v written in full when given
+};
+
+// Chunk c of the record: gather group c, or for c >= n_g the 16-token quarter
+// (c - n_g) % 4 of tile (c - n_g) / 4.  The chunk's token words start at
+// `toks`; they can be loaded before the header is checked, so that header and
+// tokens arrive in one memory round trip.
+struct Chunk {
+  bool tiles;
+  int64_t item;
+  int first;
+  const int32_t* toks;
+};
+__device__ inline Chunk chunk_at(const int32_t* rec, int T, int S, int64_t n_g, int64_t c) {
+  Chunk ch;
+  ch.tiles = c >= n_g;
+  ch.item = ch.tiles ? (c - n_g) >> 2 : c;
+  ch.first = ch.tiles ? (int)((c - n_g) & 3) * 16 : 0;
+  ch.toks = item_ptr(rec, T, S, ch.tiles, ch.item) + 4 + ch.first;
+  return ch;
+}
+// The chunk's item header (false when it does not check out) and its token
+// count (false when 0).
+__device__ inline bool chunk_header(const int32_t* rec, int T, int S, const Chunk& ch, Item& it, int& cnt) {
+  if (!read_item(rec, T, S, ch.tiles, ch.item, it)) return false;
+  cnt = min(16, it.cnt - ch.first);
+  return cnt > 0;
+}
+
+template <typename Elem>
+__global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
+  __shared__ __attribute__((aligned(1024))) char s_lds[kWaves * kFRing];
+  __shared__ int s_tok[16];
+
+  const ShrinkParams& p = f.sp;
+  const int32_t* rec = p.rec;
+  const int T = p.T, S = p.S, r_max = p.r_max, ns = p.n_slices;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool rec_ok = rec[kBuiltT] == T && rec[kBuiltS] == S;
+  int na = rec_ok ? rec[kNumActive] : 0;
+  na = na < 0 ? 0 : (na > T ? T : na);
+  const int64_t n_g = record_items(rec, T, S, false);
+  const int64_t n_chunks = n_g + 4 * record_items(rec, T, S, true);
+  const int64_t G = gridDim.x;
+
+  // K parts: enough producer units to cover the grid, at most kFusedUnits
+  // slabs, and at least one batch of two K steps per wave in every part
+  const int n_steps = (p.D + 4 * Traits<Elem>::kVec - 1) / (4 * Traits<Elem>::kVec);
+  int kp = 1;
+  if (n_chunks > 0) {
+    const int64_t want = min(G, (int64_t)kFusedUnits) / (n_chunks * ns);
+    kp = (int)max((int64_t)1, min(want, (int64_t)min(kMaxParts, max(1, n_steps / (2 * kWaves)))));
+  }
+  const int per_part = (n_steps + kp - 1) / kp;
+  const int64_t n_su = n_chunks * kp * ns;
+  const int64_t n_z = f.v_out ? ceil_div(T - na, kZeroRowsF) * ns : 0;
+  const int32_t* perm = rec + seg_layout(T, S).perm;
+  const size_t slab_floats = (size_t)16 * r_max;
+
+  // ---- producer units (then zero units) on the first workgroups, which the
+  // hardware dispatches first: a producer never waits, so the consumers below
+  // (on the last workgroups) only ever wait for work that is running or done
+  for (int64_t u = blockIdx.x; u < n_su + n_z; u += G) {
+    if (u >= n_su) {
+      // rows of tokens without an adapter: v = 0
+      const int64_t z = u - n_su;
+      const int slice = (int)(z % ns);
+      float* vb = f.v_out + (int64_t)slice * p.v_slice_stride;
+      const int w4 = r_max / 4;
+      const int64_t pos0 = na + (z / ns) * kZeroRowsF;
+      for (int e = tid; e < kZeroRowsF * w4; e += kFThreads) {
+        const int row = e / w4, c = e - row * w4;
+        const int64_t pos = pos0 + row;
+        if (pos < T) {
+          const int t = rec_ok ? perm[pos] : (int)pos;
+          if (t >= 0 && t < T) *reinterpret_cast<f32x4*>(vb + (int64_t)t * r_max + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      continue;
+    }
+    const int slice = (int)(u % ns);
+    const int part = (int)((u / ns) % kp);
+    const int64_t chunk = u / ns / kp;
+    const Chunk ch = chunk_at(rec, T, S, n_g, chunk);
+    const int tw = ch.toks[tid & 15];  // requested with the header
+    Item it;
+    int cnt;
+    if (!chunk_header(rec, T, S, ch, it, cnt)) continue;  // uniform
+    const int s = __builtin_amdgcn_readfirstlane(it.slot);
+    const int r = __builtin_amdgcn_readfirstlane(slot_rank(p.ranks, s, r_max));
+    if (r == 0) continue;  // consumers skip such chunks too
+    if (tid < 16) s_tok[tid] = tid < cnt ? (tw < 0 ? 0 : (tw >= T ? T - 1 : tw)) : -1;
+    __syncthreads();
+    const int s0 = min(n_steps, part * per_part), s1 = min(n_steps, s0 + per_part);
+    float* slab = f.part + ((slice * n_chunks + chunk) * kp + part) * slab_floats;
+    const int nb = (r + 15) / 16;
+    if (ns == 1) contract_rb<Elem, 1, true, kFRing>(p, nb, cnt, s, r, slice, s0, s1, false, slab, s_lds, s_tok, 0, r_max);
+    else contract_rb<Elem, 1, false, kFRing>(p, nb, cnt, s, r, slice, s0, s1, false, slab, s_lds, s_tok, 0, r_max);
+    // publish: every wave's slab stores are complete before the unit's count
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // also: the next unit rewrites s_tok and the rings
+    if (tid == 0)
+      __hip_atomic_fetch_add(f.counters + (slice * n_chunks + chunk) * kCounterStride, 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- consumer units: the pairs (slice, chunk, column tile) in that order,
+  // cut into equal contiguous shares; the shares of one XCD are adjacent
+  float(*s_tr)[16][kTrRow] = reinterpret_cast<float(*)[16][kTrRow]>(s_lds);  // after the rings' last use
+  const ExpandParams& e = f.ep;
+  auto n_cols = [&](int i) { return (int)ceil_div(e.out_size[i], kExpandColsPerWG); };
+  int64_t P = 0;
+  for (int i = 0; i < ns; ++i) P += n_chunks * n_cols(i);
+  const int64_t Ge = min(G, max((int64_t)kXcds, ceil_div(P, kXcds) * kXcds));
+  const int64_t ci = G - 1 - blockIdx.x;  // consumer order: the last workgroup first
+  const int64_t lb = ci / kXcds;
+  if (lb >= Ge / kXcds) return;  // uniform: no share
+  const int64_t k = (ci % kXcds) * (Ge / kXcds) + lb;  // ci % 8 names the XCD (G is a multiple of 8)
+  const int64_t w0 = P * k / Ge, w1 = P * (k + 1) / Ge;
+  int sl = 0;
+  int64_t base = 0;  // first pair of slice sl
+  const int n = lane & 15, kg = lane >> 4, yr = lane >> 3;
+  for (int64_t pos = w0; pos < w1;) {
+    while (sl < ns && pos >= base + n_chunks * n_cols(sl)) base += n_chunks * n_cols(sl++);
+    if (sl >= ns) break;
+    const int nc = n_cols(sl);
+    const int64_t chunk = (pos - base) / nc;
+    const int ct_begin = (int)((pos - base) % nc);
+    const int ct_end = (int)min((int64_t)nc, ct_begin + (w1 - pos));
+    pos += ct_end - ct_begin;
+    const Chunk ch = chunk_at(rec, T, S, n_g, chunk);
+    const int tw_n = ch.toks[n], tw_y0 = ch.toks[yr], tw_y1 = ch.toks[yr + 8];  // with the header
+    Item it;
+    int cnt;
+    if (!chunk_header(rec, T, S, ch, it, cnt)) continue;
+    auto tok = [&](int q, int t) { return q < cnt ? (t < 0 ? 0 : (t >= T ? T - 1 : t)) : -1; };
+    const int tok_n = tok(n, tw_n), ytok0 = tok(yr, tw_y0), ytok1 = tok(yr + 8, tw_y1);
+    const int s = __builtin_amdgcn_readfirstlane(it.slot);
+    const int r = __builtin_amdgcn_readfirstlane(slot_rank(e.ranks, s, r_max));
+    const bool write_v = f.v_out && ct_begin == 0 && wave == 0;
+    float* vrow = f.v_out ? f.v_out + (int64_t)sl * p.v_slice_stride + (int64_t)(tok_n >= 0 ? tok_n : 0) * r_max
+                          : nullptr;
+    if (r == 0) {
+      // rank 0: no product, v rows are zero
+      if (write_v && tok_n >= 0)
+        for (int k0 = kg * 8; k0 < r_max; k0 += 32) {
+          *reinterpret_cast<f32x4*>(vrow + k0) = f32x4{0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<f32x4*>(vrow + k0 + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      continue;
+    }
+    int32_t* cnt_ptr = f.counters + (sl * n_chunks + chunk) * kCounterStride;
+    const float* slabs = f.part + (sl * n_chunks + chunk) * kp * slab_floats + n * r_max;
+    const float sc = p.scale ? p.scale[s] : 1.0f;
+    const int nks = r > 32 ? 2 : 1;
+    const int need = kp, final_count = kp + nc, mine = ct_end - ct_begin;
+    auto vsrc = [&](f32x4 (&vraw)[2][2]) {
+      // one thread polls for the workgroup (every wave calls vsrc once per unit)
+      if (tid == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(cnt_ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+          if (++spins > kSpinLimit) {
+            atomicAdd(f.err, 1);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+      lds_barrier();  // the y and B loads stay in flight
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int k0 = ks * 32 + kg * 8;
+        const bool ok = tok_n >= 0 && ks < nks && k0 < r;
+        f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
+        if (ks < nks) {  // uniform
+          // every part's loads in flight at once, then the sum in part order
+          // (parts past kp read zeros)
+          f32x4 w[kMaxParts][2];
+#pragma unroll
+          for (int q = 0; q < kMaxParts; ++q) {
+            const bool okq = ok && q < kp;
+            const float* src = slabs + (okq ? q * slab_floats + k0 : 0);
+            w[q][0] = ldf4_or0(src, okq);
+            w[q][1] = ldf4_or0(src + 4, okq);
+          }
+#pragma unroll
+          for (int q = 0; q < kMaxParts; ++q) {
+            a0 += w[q][0];
+            a1 += w[q][1];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a0[i] = k0 + i < r ? a0[i] * sc : 0.f;
+          a1[i] = k0 + 4 + i < r ? a1[i] * sc : 0.f;
+        }
+        vraw[ks][0] = a0;
+        vraw[ks][1] = a1;
+        if (write_v && tok_n >= 0 && k0 < r_max) {
+          *reinterpret_cast<f32x4*>(vrow + k0) = a0;
+          *reinterpret_cast<f32x4*>(vrow + k0 + 4) = a1;
+        }
+      }
+    };
+    expand_group_direct<Elem>(e, vsrc, ytok0, ytok1, s_tr, sl, s, r, (int)e.out_size[sl], ct_begin, ct_end);
+    // this unit's column tiles are counted as consumed (after its y stores are
+    // issued, so the atomic's round trip overlaps them); the last consumer of
+    // the chunk sets the counter back to zero for the next call
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(cnt_ptr, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old + mine == final_count) __hip_atomic_store(cnt_ptr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <typename Elem>
+hipError_t fused_launch(const FusedParams& f, hipStream_t stream) {
+  const void* kernel = reinterpret_cast<const void*>(&fused_kernel<Elem>);
+  // the grid is what the chip holds at once: consumers wait for producers
+  const int grid = persistent_grid(kernel, kFThreads, 0, INT64_MAX / 4);
+  hipLaunchKernelGGL(fused_kernel<Elem>, dim3(grid), dim3(kFThreads), 0, stream, f);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t fused_need_bytes(int64_t T, int64_t S, int64_t n_slices, int64_t r_max) {
+  const SegLayout L = seg_layout(T, S);
+  const int64_t units = n_slices * (L.cap_groups + 4 * L.cap_tiles);  // counters
+  const int64_t slabs = (units > kFusedUnits ? units : kFusedUnits) * 16 * r_max * 4;
+  const int64_t v_bytes = n_slices * T * r_max * 4;  // v of the two-launch form
+  const int64_t data = slabs > v_bytes ? slabs : v_bytes;
+  // the counter region is a quarter of the whole, at least 128 bytes per
+  // counter; the rest holds the data after 512 bytes of header and alignment
+  int64_t b = ceil_div((data + 512) * 4, 3);
+  if (b < 4 * 128 * (units + 1)) b = 4 * 128 * (units + 1);
+  return (b + 255) & ~int64_t(255);
+}
+
+FusedLayout fused_layout(int64_t bytes) {
+  FusedLayout W;
+  W.counters = 256;
+  W.counter_bytes = (bytes / 4) & ~int64_t(127);
+  W.part = (W.counters + W.counter_bytes + 255) & ~int64_t(255);
+  return W;
+}
+
+hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, char* ws,
+                        int64_t ws_bytes, float* v_out, hipStream_t stream) {
+  const FusedLayout W = fused_layout(ws_bytes);
+  FusedParams f;
+  f.sp = sp;
+  f.ep = ep;
+  f.part = reinterpret_cast<float*>(ws + W.part);
+  f.counters = reinterpret_cast<int32_t*>(ws + W.counters);
+  f.err = reinterpret_cast<int32_t*>(ws);
+  f.v_out = v_out;
+  switch (dt) {
+    case LORA_F16: return fused_launch<half_t>(f, stream);
+    case LORA_BF16: return fused_launch<bf16_t>(f, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lora

@@ -204,6 +204,49 @@ lora_status lora_expand(lora_dtype dt, const float *v, int64_t v_slice_stride, i
                         const int32_t *ranks, const void *seg, int32_t active_hint, void *y,
                         int64_t ldy, hipStream_t stream);
 
+/*
+ * Shrink then expand of one layer in a single call: the result of lora_shrink
+ * followed by lora_expand with v_slice_stride = T * r_max (the shrink and
+ * expand of "Add multi-LoRA support", with the fp32 intermediate its
+ * Limitations ask for), for decode-shaped batches whose layers are dominated
+ * by launch and memory latency rather than by bytes.
+ *   x, ldx, D, A, scale          as lora_shrink
+ *   B, out_sizes, out_offsets    as lora_expand; y, ldy as lora_expand
+ *   v          nullable; [n_slices][T][r_max] fp32 device.  When given it is
+ *              written in full, exactly as lora_shrink writes it.
+ *   workspace  device memory of workspace_bytes >=
+ *              lora_shrink_expand_workspace_bytes(T, S, n_slices, r_max)
+ *              bytes, 256-byte aligned, owned by the caller; pass the same
+ *              workspace_bytes with it every time (its layout depends only on
+ *              that size).  Clear the whole workspace once after allocating it:
+ *              its header and counters must be zero when a call starts, and
+ *              every call leaves them zero again, so calls in stream order, of
+ *              any shape that fits, can share one workspace.  Calls that may
+ *              overlap (other streams) need distinct workspaces.  int32 word 0
+ *              counts device-side waits that gave up (0 in every normal run;
+ *              if it is not 0 the call's output is invalid and the workspace
+ *              must be cleared again).
+ * fp16/bf16 batches of T <= lora_fused_max_tokens() run as one launch:
+ * producer work units shrink 16-token chunks over ranges of D into the
+ * workspace and consumer units expand each chunk once every part of it is
+ * there.  Larger batches and fp32 run as the shrink launch and the expand
+ * launch, with v in the workspace when v is NULL.
+ * Errors and the no-op gate are those of lora_shrink and lora_expand, plus
+ * LORA_ERR_INVALID_ARG for a null, misaligned or short workspace.
+ */
+size_t lora_shrink_expand_workspace_bytes(int32_t T, int32_t S, int32_t n_slices, int32_t r_max);
+
+/* Largest T that lora_shrink_expand runs as one launch (16-bit data). */
+int32_t lora_fused_max_tokens(void);
+
+lora_status lora_shrink_expand(lora_dtype dt, const void *x, int64_t ldx, int32_t T, int32_t D,
+                               int32_t n_slices, const void *const *A, const void *const *B,
+                               const int64_t *out_sizes, const int64_t *out_offsets, int32_t S,
+                               int32_t r_max, const int32_t *ranks, const float *scale,
+                               const void *seg, int32_t active_hint, float *v, void *y,
+                               int64_t ldy, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                              */
 /* ------------------------------------------------------------------------ */

@@ -37,11 +37,34 @@ def rel_err(got, ref):
     return num / den
 
 
-def run_gpu(p, *, mode="auto", device="cuda", shared_v=False):
+def fused_counter_bytes(ws):
+    """Bytes at the start of a shrink_expand workspace that every call leaves
+    zero: the 256-byte header and the counter region (the workspace's first
+    quarter, after the header)."""
+    return 256 + ws.numel() // 4
+
+
+def run_fused(p, d, seg, ws=None):
+    """shrink_expand on device tensors d; checks the workspace is left clean."""
+    v = torch.full((p.n_slices, p.T, p.r_max), float("nan"), dtype=torch.float32, device=d["x"].device)
+    if ws is None:
+        ws = glsa.alloc_workspace(p.T, p.S, p.n_slices, p.r_max, d["x"].device)
+    glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], seg, p.out_offsets, workspace=ws,
+                       scale=d["scale"], ranks=d["ranks"], v=v)
+    torch.cuda.synchronize()
+    assert glsa.workspace_errors(ws) == 0, "a fused wait gave up"
+    if p.dtype != "f32" and p.T > 0:
+        assert not torch.any(ws[:fused_counter_bytes(ws)]).item(), "fused counters not back at zero"
+    return v
+
+
+def run_gpu(p, *, mode="auto", device="cuda", shared_v=False, fused=False):
     """Build segments, shrink and expand on the GPU.  Returns (v, y, info)."""
     d = problem_to_device(p, device)
     seg = glsa.build_segments(d["idx"], p.S, mode=mode)
-    if shared_v:
+    if fused:
+        v = run_fused(p, d, seg)
+    elif shared_v:
         v = glsa.shrink(d["x"], d["A"][:1], seg, scale=d["scale"], ranks=d["ranks"])
         glsa.expand(v, d["B"], d["y"], seg, p.out_offsets, ranks=d["ranks"], v_slice_stride=0)
     else:
@@ -63,7 +86,7 @@ def oracle_ref(p, tokens=None, shared_v=False):
     return v, y
 
 
-def check_problem(p, *, mode="auto", tokens=None, shared_v=False, label=""):
+def check_problem(p, *, mode="auto", tokens=None, shared_v=False, fused=False, label=""):
     """Run the GPU path on p and assert parity with the oracle.
 
     tokens: None compares every row; otherwise only those rows are compared
@@ -71,8 +94,8 @@ def check_problem(p, *, mode="auto", tokens=None, shared_v=False, label=""):
     bit-identical, v zero outside active rows/ranks) are checked on all rows.
     """
     say(f"[parity] {label} dtype={p.dtype} T={p.T} D={p.D} S={p.S} r_max={p.r_max} "
-        f"slices={p.out_sizes} mode={mode}")
-    v_gpu, y_gpu, info = run_gpu(p, mode=mode, shared_v=shared_v)
+        f"slices={p.out_sizes} mode={mode}{' fused' if fused else ''}")
+    v_gpu, y_gpu, info = run_gpu(p, mode=mode, shared_v=shared_v, fused=fused)
     rows = np.arange(p.T) if tokens is None else np.asarray(tokens)
     v_ref, y_ref = oracle_ref(p, tokens=None if tokens is None else rows, shared_v=shared_v)
     y_got = oracle.decode(y_gpu[rows], p.dtype)

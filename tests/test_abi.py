@@ -165,3 +165,61 @@ def test_build_segments_rejects_bad_arguments():
 def test_python_binding_raises_lora_error():
     err = glsa.LoraError(glsa.LORA_ERR_INDEX, "x")
     assert err.status == 3 and "LORA_ERR_INDEX" in str(err)
+
+
+# --------------------------------------------------------------------------
+# lora_shrink_expand: host-side checks (no GPU call)
+# --------------------------------------------------------------------------
+
+def _fused(**kw):
+    a = dict(dt=1, x=FAKE, ldx=64, T=8, D=64, n_slices=1, A=[FAKE], B=[FAKE], sizes=[64],
+             offs=[0], S=4, r_max=16, ranks=None, scale=None, seg=FAKE, active=1, v=None,
+             y=FAKE, ldy=64, ws=FAKE, ws_bytes=None)
+    a.update(kw)
+    n = a["n_slices"]
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = glsa.workspace_bytes(a["T"], a["S"], n, a["r_max"]) if a["T"] >= 0 else 0
+    A = (ctypes.c_void_p * len(a["A"]))(*a["A"])
+    B = (ctypes.c_void_p * len(a["B"]))(*a["B"])
+    sizes = (ctypes.c_int64 * len(a["sizes"]))(*a["sizes"])
+    offs = (ctypes.c_int64 * len(a["offs"]))(*a["offs"])
+    return glsa.lib().lora_shrink_expand(a["dt"], a["x"], a["ldx"], a["T"], a["D"], n, A, B, sizes,
+                                         offs, a["S"], a["r_max"], a["ranks"], a["scale"], a["seg"],
+                                         a["active"], a["v"], a["y"], a["ldy"], a["ws"],
+                                         a["ws_bytes"], None)
+
+
+def test_fused_workspace_bytes():
+    # header + one counter per slice and 16-token chunk + the producer slabs
+    for T, S, n, r in [(1, 1, 1, 8), (256, 8, 1, 16), (8192, 16, 3, 64), (1024, 32, 2, 64)]:
+        b = glsa.workspace_bytes(T, S, n, r)
+        assert b % 256 == 0 and b >= 256 + 1024 * 16 * r * 4 * 4 // 3
+        assert b >= 256 + n * T * r * 4  # room for v in the two-launch (fp32) form
+    assert glsa.workspace_bytes(-1, 4, 1, 8) == 0
+    assert glsa.workspace_bytes(4, 4, 9, 8) == 0
+    assert glsa.workspace_bytes(4, 4, 1, 72) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 16), glsa.LORA_ERR_INVALID_ARG),   # not 256-byte aligned
+    (dict(ws_bytes=1024), glsa.LORA_ERR_INVALID_ARG),  # too small
+    (dict(dt=5), glsa.LORA_ERR_INVALID_ARG),
+    (dict(x=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(y=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(D=60, ldx=64), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(sizes=[8], offs=[64]), glsa.LORA_ERR_INVALID_ARG),  # ends past ldy
+    (dict(v=FAKE + 8), glsa.LORA_ERR_UNSUPPORTED),      # misaligned v
+    (dict(A=[0]), glsa.LORA_ERR_INVALID_ARG),
+    (dict(B=[0]), glsa.LORA_ERR_INVALID_ARG),
+])
+def test_fused_rejects_bad_arguments(kw, status):
+    assert _fused(**kw) == status
+    assert glsa.lib().lora_last_error()
+
+
+def test_fused_inactive_and_empty_are_host_side_no_ops():
+    assert _fused(active=0) == glsa.LORA_OK
+    assert _fused(active=0, v=FAKE) == glsa.LORA_OK
+    assert _fused(T=0) == glsa.LORA_OK
+    assert _fused(active=0, D=0) == glsa.LORA_ERR_INVALID_ARG  # still validated first

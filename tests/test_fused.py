@@ -1,0 +1,142 @@
+"""GPU: the one-call shrink_expand (one launch for 16-bit data) matches the fp64
+oracle to the same bars as shrink followed by expand, on the five workloads
+and the edge cases; it leaves its workspace's counters at zero after every
+call, so one workspace serves calls in stream order on batches of any shape;
+and a captured step with it replays correctly."""
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_lora_shrink_amd as glsa
+import oracle
+from gpu_util import (V_TOL, Y_TOL, check_problem, oracle_ref, rel_err, run_fused,
+                      sample_tokens, say)
+from test_parity import edge_problems
+from workloads import make_workload, random_problem
+from workloads.torch_io import from_torch, problem_to_device
+
+pytestmark = pytest.mark.gpu
+
+FULL = [("tiny_bgmv", None), ("decode_qproj", None), ("prefill_qkv", 256),
+        ("mixed_rank_mlp", None), ("zipf_many", 512)]
+
+
+@pytest.mark.parametrize("name,n_sample", FULL, ids=[f[0] for f in FULL])
+def test_fused_workload_parity(name, n_sample):
+    wl = make_workload(name)
+    for p in wl.problems:
+        tokens = None if n_sample is None else sample_tokens(p.idx, p.S, n_sample)
+        check_problem(p, tokens=tokens, fused=True, label=f"fused/{name}/{p.name}")
+
+
+@pytest.mark.parametrize("case", list(edge_problems()), ids=lambda c: c[0])
+def test_fused_edge_parity(case):
+    label, p, mode = case
+    if p.ranks is not None:  # garbage in the rank padding must be ignored
+        for s, r in enumerate(p.ranks):
+            for a in p.A:
+                a[s, r:, :] = a.dtype.type(7) if a.dtype != np.uint16 else np.uint16(0x40e0)
+            for b in p.B:
+                b[s, :, r:] = b.dtype.type(7) if b.dtype != np.uint16 else np.uint16(0x40e0)
+    check_problem(p, mode=mode, fused=True, label=f"fused/{label}")
+
+
+def test_fused_workspace_reuse_across_batches():
+    """One workspace for calls in stream order on batches of different sizes,
+    slices and ranks, twice over: each call matches the oracle and leaves the
+    counters at zero (checked inside run_fused)."""
+    rng = np.random.default_rng(21)
+    probs = [
+        random_problem(rng, T=512, D=512, out_sizes=(256, 128), r_max=32, S=8, dtype="f16",
+                       with_ranks=True),
+        random_problem(rng, T=100, D=256, out_sizes=(128,), r_max=16, S=4, dtype="bf16"),
+        random_problem(rng, T=700, D=1024, out_sizes=(64, 64, 64), r_max=64, S=40, dtype="bf16"),
+        random_problem(rng, T=20, D=64, out_sizes=(32,), r_max=8, S=3, dtype="f16"),
+    ]
+    size = max(glsa.workspace_bytes(p.T, p.S, p.n_slices, p.r_max) for p in probs)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for rnd in range(2):
+        for i, p in enumerate(probs):
+            say(f"[fused reuse] round {rnd} problem {i} T={p.T} slices={p.out_sizes} r_max={p.r_max}")
+            d = problem_to_device(p, "cuda")
+            seg = glsa.build_segments(d["idx"], p.S)
+            v = run_fused(p, d, seg, ws=ws)
+            v_ref, y_ref = oracle_ref(p)
+            y = oracle.decode(from_torch(d["y"], p.dtype), p.dtype)
+            assert rel_err(y, y_ref) <= Y_TOL[p.dtype]
+            assert rel_err(v.cpu().numpy(), v_ref) <= V_TOL
+
+
+def test_fused_inactive_hint_enqueues_nothing():
+    rng = np.random.default_rng(5)
+    p = random_problem(rng, T=64, D=64, out_sizes=(64,), r_max=8, S=2, dtype="bf16", base_frac=1.0)
+    d = problem_to_device(p, "cuda")
+    seg = glsa.build_segments(d["idx"], p.S)
+    ws = glsa.alloc_workspace(p.T, p.S, p.n_slices, p.r_max, "cuda")
+    y0 = d["y"].clone()
+    v = torch.full((1, p.T, p.r_max), 3.0, device="cuda")
+    glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], seg, p.out_offsets, workspace=ws, v=v,
+                       active=False)
+    torch.cuda.synchronize()
+    assert torch.equal(d["y"], y0) and bool(torch.all(v == 3.0)) and not torch.any(ws).item()
+
+
+@pytest.mark.parametrize("name", ["decode_qproj", "mixed_rank_mlp"])
+def test_fused_graph_replays(name):
+    """Segment build + shrink_expand captured once and replayed 4 times, with
+    the program's own eager work (y reset, v poisoned) and a synchronisation
+    between replays; each replay matches the eager run and the oracle."""
+    wl = make_workload(name)
+    probs = wl.problems
+    ds = [problem_to_device(p, "cuda") for p in probs]
+    seg = glsa.alloc_segments(wl.T, wl.S, "cuda")
+    vs = [torch.empty((p.n_slices, wl.T, p.r_max), dtype=torch.float32, device="cuda") for p in probs]
+    wss = [glsa.alloc_workspace(p.T, p.S, p.n_slices, p.r_max, "cuda") for p in probs]
+    y_in = [d["y"].clone() for d in ds]
+
+    def step():
+        glsa.build_segments(ds[0]["idx"], wl.S, seg=seg)
+        for p, d, v, ws in zip(probs, ds, vs, wss):
+            glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], seg, p.out_offsets, workspace=ws,
+                               scale=d["scale"], ranks=d["ranks"], v=v)
+
+    def reset():
+        for d, y0 in zip(ds, y_in):
+            d["y"].copy_(y0)
+        for v in vs:
+            v.fill_(float("nan"))
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    y_eager = [oracle.decode(from_torch(d["y"], p.dtype), p.dtype) for p, d in zip(probs, ds)]
+    rows = sample_tokens(wl.idx, wl.S, 64)
+    refs = [oracle_ref(p, tokens=rows) for p in probs]
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        reset()
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say(f"[fused graph] {name} replay {rep}")
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for li, (p, d, v, ws) in enumerate(zip(probs, ds, vs, wss)):
+            assert glsa.workspace_errors(ws) == 0
+            vg = v.cpu().numpy().astype(np.float64)
+            yg = oracle.decode(from_torch(d["y"], p.dtype), p.dtype)
+            assert np.all(np.isfinite(vg)), f"{name} replay {rep}: v not fully written"
+            assert rel_err(yg, y_eager[li]) <= Y_TOL[p.dtype] / 2
+            v_ref, y_ref = refs[li]
+            assert rel_err(vg[:, rows], v_ref) <= V_TOL
+            assert rel_err(yg[rows], y_ref) <= Y_TOL[p.dtype]
