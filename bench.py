@@ -3,6 +3,10 @@
 
 A step is one pass of the whole path over one batch: the segment build, then
 for every LoRA layer of the workload its shrink and (where timed) its expand.
+By default each layer with a timed expand is one shrink_expand call.  With
+--overlap the first such call groups the tokens itself and the segment record
+(which the later layers read) is built beside it on a second stream, inside
+the same step.
 Inputs are resident in HBM before timing starts.  Steps rotate over several
 device copies of the inputs, enough that the working set exceeds the 256 MB
 last-level cache, so the byte rates below are HBM rates, not cache rates.
@@ -44,6 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
+    ap.add_argument("--overlap", action="store_true",
+                    help="build the segment record on a second stream beside the first layer, which "
+                         "then groups the tokens itself (measured slower on MI355X: off by default)")
     ap.add_argument("--eager", action="store_true", help="time host launches instead of graph replay")
     ap.add_argument("--path", default="fused", choices=["fused", "split"],
                     help="fused: each layer with a timed expand is one shrink_expand call (one "
@@ -228,23 +235,40 @@ def main():
         glsa.expand(d["v"], d["B"], d["y"], st["seg"], p.out_offsets, ranks=d["ranks"],
                     active=active)
 
+    fused = args.path == "fused"
+    # The first layer of a batch needs no segment record when its shrink_expand
+    # runs as one launch and groups the tokens itself from idx: the record for
+    # the later layers is then built on a side stream at the same time.
+    overlap = (fused and args.overlap and problems[0].timed_expand
+               and wl.dtype in ("f16", "bf16") and T <= glsa.fused_max_tokens())
+
     def do_fused(st, li):
         d, p = st["layers"][li], problems[li]
         glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], st["seg"], p.out_offsets,
                            workspace=d["ws"], scale=d["scale"], ranks=d["ranks"], v=d["v"],
-                           active=active)
+                           idx=st["idx"] if overlap and li == 0 else None, active=active)
 
-    fused = args.path == "fused"
+    side = torch.cuda.Stream()
 
     def step(st):
-        do_segments(st)
+        main = torch.cuda.current_stream()
+        if overlap:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                do_segments(st)
+        else:
+            do_segments(st)
         for li, p in enumerate(problems):
+            if overlap and li == 1:
+                main.wait_stream(side)  # later layers read the record
             if fused and p.timed_expand:
                 do_fused(st, li)
                 continue
             do_shrink(st, li)
             if p.timed_expand:
                 do_expand(st, li)
+        if overlap:
+            main.wait_stream(side)
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
@@ -368,7 +392,8 @@ def main():
                     layers=[dict(name=p.name, D=p.D, out=list(p.out_sizes),
                                  timed_expand=p.timed_expand) for p in problems],
                     n_active=alg[0]["n_active"], n_distinct_slots=alg[0]["n_distinct"],
-                    mode=args.mode, path=args.path, timing=timed_mode, input_sets=n_sets,
+                    mode=args.mode, path=args.path, record_beside_first_layer=overlap,
+                    timing=timed_mode, input_sets=n_sets,
                     accumulate="fp32"),
         step_gbs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         step_tflops=round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),

@@ -78,7 +78,7 @@ def _load():
     lib.lora_shrink_expand_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.lora_shrink_expand_workspace_bytes.restype = sz
     lib.lora_shrink_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp, i32,
-                                       i32, vp, vp, vp, i32, vp, vp, i64, vp, sz, vp]
+                                       i32, vp, vp, vp, vp, i32, vp, vp, i64, vp, sz, vp]
     lib.lora_shrink_expand.restype = ctypes.c_int
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
@@ -260,10 +260,12 @@ def workspace_errors(ws):
 
 
 def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=None, v=None,
-                  active=True, stream=None):
+                  idx=None, active=True, stream=None):
     """Shrink then expand in one call; y updated in place.  Returns y.
 
     v (optional, [n_slices, T, r_max] float32) receives the intermediate.
+    idx (optional, int32 [T]): when given, a one-launch call groups the tokens
+    itself and does not read seg.
     workspace: from alloc_workspace (zeroed once; every call leaves it reusable).
     """
     A, B = list(A), list(B)
@@ -283,6 +285,9 @@ def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=
     if v is not None and (v.dtype != torch.float32 or not v.is_contiguous()
                           or v.shape != (len(A), T, r_max)):
         raise LoraError(LORA_ERR_INVALID_ARG, "v must be contiguous float32 [n_slices, T, r_max]")
+    if idx is not None and (idx.dtype != torch.int32 or idx.dim() != 1 or not idx.is_contiguous()
+                            or idx.numel() != T):
+        raise LoraError(LORA_ERR_INVALID_ARG, "idx must be a contiguous int32 tensor of T entries")
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise LoraError(LORA_ERR_INVALID_ARG, "workspace must be a contiguous uint8 tensor")
     n = len(A)
@@ -291,7 +296,8 @@ def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=
     sizes = (ctypes.c_int64 * n)(*[b.shape[1] for b in B])
     offs = (ctypes.c_int64 * n)(*[int(o) for o in out_offsets])
     st = _load().lora_shrink_expand(_dtype_code(x), _ptr(x), ldx, T, D, n, a_ptrs, b_ptrs, sizes, offs,
-                                    S, r_max, _ptr(ranks), _ptr(scale), _ptr(seg), 1 if active else 0,
+                                    S, r_max, _ptr(ranks), _ptr(scale), _ptr(seg), _ptr(idx),
+                                    1 if active else 0,
                                     _ptr(v), _ptr(y), ldy, _ptr(workspace), workspace.numel(),
                                     _stream(stream, x.device))
     _check(st)

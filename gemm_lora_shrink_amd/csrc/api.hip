@@ -329,7 +329,8 @@ LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t
                                            int32_t n_slices, const void* const* A, const void* const* B,
                                            const int64_t* out_sizes, const int64_t* out_offsets, int32_t S,
                                            int32_t r_max, const int32_t* ranks, const float* scale, const void* seg,
-                                           int32_t active_hint, float* v, void* y, int64_t ldy, void* workspace,
+                                           const int32_t* idx, int32_t active_hint, float* v, void* y, int64_t ldy,
+                                           void* workspace,
                                            size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
@@ -355,7 +356,7 @@ LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t
   if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
   hipError_t e;
   if (dt != LORA_F32 && T <= kFusedMaxTokens) {
-    e = launch_fused(dt, sp, ep, ws, (int64_t)workspace_bytes, v, stream);
+    e = launch_fused(dt, sp, ep, idx, ws, (int64_t)workspace_bytes, v, stream);
   } else {
     // larger batches stream enough bytes per launch that the launch and the
     // round trips no longer dominate: the shrink launch then the expand launch

@@ -325,9 +325,11 @@ struct FusedLayout {
 FusedLayout fused_layout(int64_t bytes);
 // Smallest workspace for a call of this shape.
 int64_t fused_need_bytes(int64_t T, int64_t S, int64_t n_slices, int64_t r_max);
-// Shrink and expand of the record's items in one launch (16-bit types only);
-// v_out (nullable) receives v in full.
-hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, char* ws,
+// Shrink and expand of the batch's 16-token chunks in one launch (16-bit types
+// only); v_out (nullable) receives v in full.
+// idx (nullable): the batch's slots; when given, the kernel groups the tokens
+// itself (T <= kFusedMaxTokens) and does not read the segment record.
+hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, const int32_t* idx, char* ws,
                         int64_t ws_bytes, float* v_out, hipStream_t stream);
 
 }  // namespace lora

@@ -60,7 +60,45 @@ struct FusedParams {
   int32_t* counters;  // [n_slices * chunk_cap]
   int32_t* err;       // waits that gave up
   float* v_out;       // nullable: v written in full when given
+  const int32_t* idx; // the batch's slots: grouped in each workgroup (idx mode)
 };
+
+// idx mode: every workgroup groups the batch's tokens by slot itself, in LDS,
+// from idx (T <= kFusedMaxTokens): tokens per slot and the first chunk of each
+// slot.  A slot's chunks are its tokens, in token order, cut into runs of 16
+// (the same pieces as the record's gather groups and tile quarters).
+constexpr int kTokPerThread = kFusedMaxTokens / kFThreads;
+static_assert(kTokPerThread * kFThreads == kFusedMaxTokens, "tokens per thread");
+struct IdxTables {
+  int cnt[LORA_MAX_SLOTS];      // tokens per slot
+  int cst[LORA_MAX_SLOTS + 1];  // first chunk of each slot; [S] = chunks
+  int scan[kWaves];
+  int slot;
+};
+
+// Exclusive prefix sum of v over the workgroup's threads (thread order), and
+// the total.  Every thread calls it.
+__device__ inline int block_exscan(int v, int* scan, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) scan[wave] = x;
+  lds_barrier();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = scan[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  lds_barrier();  // scan may be rewritten
+  return before + x - v;
+}
 
 // Chunk c of the record: gather group c, or for c >= n_g the 16-token quarter
 // (c - n_g) % 4 of tile (c - n_g) / 4.  The chunk's token words start at
@@ -88,21 +126,94 @@ __device__ inline bool chunk_header(const int32_t* rec, int T, int S, const Chun
   return cnt > 0;
 }
 
-template <typename Elem>
+template <typename Elem, bool FROM_IDX>
 __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   __shared__ __attribute__((aligned(1024))) char s_lds[kWaves * kFRing];
   __shared__ int s_tok[16];
+  __shared__ IdxTables s_it;
 
   const ShrinkParams& p = f.sp;
   const int32_t* rec = p.rec;
   const int T = p.T, S = p.S, r_max = p.r_max, ns = p.n_slices;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool rec_ok = rec[kBuiltT] == T && rec[kBuiltS] == S;
-  int na = rec_ok ? rec[kNumActive] : 0;
-  na = na < 0 ? 0 : (na > T ? T : na);
-  const int64_t n_g = record_items(rec, T, S, false);
-  const int64_t n_chunks = n_g + 4 * record_items(rec, T, S, true);
   const int64_t G = gridDim.x;
+  bool rec_ok = false;
+  int na = 0;
+  int64_t n_g = 0, n_chunks = 0;
+  // idx mode: this thread's tokens t_first .. t_first + kTokPerThread - 1 and
+  // their slots (-1: no valid slot)
+  const int t_first = tid * kTokPerThread;
+  int keys[kTokPerThread];
+  if constexpr (FROM_IDX) {
+#pragma unroll
+    for (int i = 0; i < kTokPerThread; ++i) {
+      const int t = t_first + i;
+      const int k = t < T ? f.idx[t] : -1;
+      keys[i] = k >= 0 && k < S ? k : -1;
+    }
+    for (int s = tid; s < S; s += kFThreads) s_it.cnt[s] = 0;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < kTokPerThread; ++i)
+      if (keys[i] >= 0) atomicAdd(&s_it.cnt[keys[i]], 1);
+    lds_barrier();
+    // chunks per slot, scanned over the slots (4 slots per thread)
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 4 * tid + j;
+      local += s < S ? (s_it.cnt[s] + 15) >> 4 : 0;
+    }
+    int total;
+    int ex = block_exscan(local, s_it.scan, total);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 4 * tid + j;
+      if (s < S) {
+        s_it.cst[s] = ex;
+        ex += (s_it.cnt[s] + 15) >> 4;
+      }
+    }
+    if (tid == 0) s_it.cst[S] = total;
+    lds_barrier();
+    n_chunks = total;
+  } else {
+    rec_ok = rec[kBuiltT] == T && rec[kBuiltS] == S;
+    na = rec_ok ? rec[kNumActive] : 0;
+    na = na < 0 ? 0 : (na > T ? T : na);
+    n_g = record_items(rec, T, S, false);
+    n_chunks = n_g + 4 * record_items(rec, T, S, true);
+  }
+  // idx mode: the slot, token count and tokens (into s_tok) of chunk c; every
+  // thread calls it
+  auto idx_chunk = [&](int64_t c, int& s, int& cnt) {
+    lds_barrier();  // the previous chunk's s_tok and slot are no longer read
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = 4 * tid + j;
+      if (q < S) {
+        const int nch = (s_it.cnt[q] + 15) >> 4;
+        if (nch > 0 && s_it.cst[q] <= c && c < s_it.cst[q] + nch) s_it.slot = q;
+      }
+    }
+    if (tid < 16) s_tok[tid] = -1;
+    lds_barrier();
+    s = __builtin_amdgcn_readfirstlane(s_it.slot);
+    const int piece = (int)(c - s_it.cst[s]);
+    cnt = min(16, s_it.cnt[s] - 16 * piece);
+    int m = 0;
+#pragma unroll
+    for (int i = 0; i < kTokPerThread; ++i) m += keys[i] == s ? 1 : 0;
+    int tot;
+    int rk = block_exscan(m, s_it.scan, tot) - 16 * piece;  // rank of this thread's first match in the chunk
+#pragma unroll
+    for (int i = 0; i < kTokPerThread; ++i)
+      if (keys[i] == s) {
+        if (rk >= 0 && rk < 16) s_tok[rk] = t_first + i;
+        ++rk;
+      }
+    lds_barrier();
+  };
 
   // K parts: enough producer units to cover the grid, at most kFusedUnits
   // slabs, and at least one batch of two K steps per wave in every part
@@ -114,7 +225,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   }
   const int per_part = (n_steps + kp - 1) / kp;
   const int64_t n_su = n_chunks * kp * ns;
-  const int64_t n_z = f.v_out ? ceil_div(T - na, kZeroRowsF) * ns : 0;
+  const int64_t n_z = f.v_out ? ceil_div(FROM_IDX ? T : T - na, kZeroRowsF) * ns : 0;
   const int32_t* perm = rec + seg_layout(T, S).perm;
   const size_t slab_floats = (size_t)16 * r_max;
 
@@ -132,7 +243,16 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       for (int e = tid; e < kZeroRowsF * w4; e += kFThreads) {
         const int row = e / w4, c = e - row * w4;
         const int64_t pos = pos0 + row;
-        if (pos < T) {
+        if (FROM_IDX) {
+          // idx mode: unit z covers token rows 64 z .. 64 z + 63; those
+          // without a valid slot are cleared
+          const int64_t t = (z / ns) * kZeroRowsF + row;
+          if (t < T) {
+            const int k = f.idx[t];
+            if (k < 0 || k >= S)
+              *reinterpret_cast<f32x4*>(vb + t * r_max + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        } else if (pos < T) {
           const int t = rec_ok ? perm[pos] : (int)pos;
           if (t >= 0 && t < T) *reinterpret_cast<f32x4*>(vb + (int64_t)t * r_max + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -142,16 +262,20 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
     const int slice = (int)(u % ns);
     const int part = (int)((u / ns) % kp);
     const int64_t chunk = u / ns / kp;
-    const Chunk ch = chunk_at(rec, T, S, n_g, chunk);
-    const int tw = ch.toks[tid & 15];  // requested with the header
-    Item it;
-    int cnt;
-    if (!chunk_header(rec, T, S, ch, it, cnt)) continue;  // uniform
-    const int s = __builtin_amdgcn_readfirstlane(it.slot);
+    int s, cnt;
+    if constexpr (FROM_IDX) {
+      idx_chunk(chunk, s, cnt);
+    } else {
+      const Chunk ch = chunk_at(rec, T, S, n_g, chunk);
+      const int tw = ch.toks[tid & 15];  // requested with the header
+      Item it;
+      if (!chunk_header(rec, T, S, ch, it, cnt)) continue;  // uniform
+      s = __builtin_amdgcn_readfirstlane(it.slot);
+      if (tid < 16) s_tok[tid] = tid < cnt ? (tw < 0 ? 0 : (tw >= T ? T - 1 : tw)) : -1;
+      __syncthreads();
+    }
     const int r = __builtin_amdgcn_readfirstlane(slot_rank(p.ranks, s, r_max));
     if (r == 0) continue;  // consumers skip such chunks too
-    if (tid < 16) s_tok[tid] = tid < cnt ? (tw < 0 ? 0 : (tw >= T ? T - 1 : tw)) : -1;
-    __syncthreads();
     const int s0 = min(n_steps, part * per_part), s1 = min(n_steps, s0 + per_part);
     float* slab = f.part + ((slice * n_chunks + chunk) * kp + part) * slab_floats;
     const int nb = (r + 15) / 16;
@@ -165,38 +289,70 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
                              __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- consumer units: the pairs (slice, chunk, column tile) in that order,
-  // cut into equal contiguous shares; the shares of one XCD are adjacent
+  // ---- consumer units: the pairs (slice, chunk, column tile), cut into equal
+  // contiguous shares, the shares of one XCD adjacent.  Each slice's column
+  // tiles are cut into blocks of C, and pairs are ordered by slice, block,
+  // chunk, column tile.  C is a whole slice unless the B rows of the slots one
+  // XCD sees would not stay in its L2; then C is about the pairs per share, so
+  // that the chunks of one slot, which read the same B rows, are taken at
+  // about the same time by workgroups of one XCD.
   float(*s_tr)[16][kTrRow] = reinterpret_cast<float(*)[16][kTrRow]>(s_lds);  // after the rings' last use
   const ExpandParams& e = f.ep;
   auto n_cols = [&](int i) { return (int)ceil_div(e.out_size[i], kExpandColsPerWG); };
-  int64_t P = 0;
-  for (int i = 0; i < ns; ++i) P += n_chunks * n_cols(i);
+  int64_t P = 0, max_out = 0;
+  int max_cols = 1;
+  for (int i = 0; i < ns; ++i) {
+    P += n_chunks * n_cols(i);
+    max_cols = max(max_cols, n_cols(i));
+    max_out = max(max_out, e.out_size[i]);
+  }
   const int64_t Ge = min(G, max((int64_t)kXcds, ceil_div(P, kXcds) * kXcds));
   const int64_t ci = G - 1 - blockIdx.x;  // consumer order: the last workgroup first
   const int64_t lb = ci / kXcds;
   if (lb >= Ge / kXcds) return;  // uniform: no share
   const int64_t k = (ci % kXcds) * (Ge / kXcds) + lb;  // ci % 8 names the XCD (G is a multiple of 8)
   const int64_t w0 = P * k / Ge, w1 = P * (k + 1) / Ge;
-  int sl = 0;
-  int64_t base = 0;  // first pair of slice sl
+  // distinct slots in the batch (idx mode: at most the chunks and the slots)
+  const int64_t n_seg = FROM_IDX ? max((int64_t)1, min((int64_t)S, n_chunks)) : max(1, rec[kNumSegments]);
+  const bool blocked = ceil_div(n_seg, kXcds) * max_out * r_max * (int64_t)sizeof(Elem) > (int64_t)(4 << 20);
+  const int C = blocked ? (int)min((int64_t)max_cols, max((int64_t)1, ceil_div(P, Ge))) : max_cols;
+  int sl = 0, c0 = 0;  // current block: slice sl, column tiles c0 .. c0 + width - 1
+  int64_t base = 0;    // first pair of the block
+  auto width = [&]() { return min(C, n_cols(sl) - c0); };
+  auto next_block = [&]() {
+    base += n_chunks * width();
+    c0 += C;
+    if (c0 >= n_cols(sl)) {
+      c0 = 0;
+      ++sl;
+    }
+  };
   const int n = lane & 15, kg = lane >> 4, yr = lane >> 3;
   for (int64_t pos = w0; pos < w1;) {
-    while (sl < ns && pos >= base + n_chunks * n_cols(sl)) base += n_chunks * n_cols(sl++);
+    while (sl < ns && pos >= base + n_chunks * width()) next_block();
     if (sl >= ns) break;
-    const int nc = n_cols(sl);
-    const int64_t chunk = (pos - base) / nc;
-    const int ct_begin = (int)((pos - base) % nc);
-    const int ct_end = (int)min((int64_t)nc, ct_begin + (w1 - pos));
+    const int nc = n_cols(sl), cb = width();
+    const int64_t chunk = (pos - base) / cb;
+    const int ct_begin = c0 + (int)((pos - base) % cb);
+    const int ct_end = (int)min((int64_t)c0 + cb, ct_begin + (w1 - pos));
     pos += ct_end - ct_begin;
-    const Chunk ch = chunk_at(rec, T, S, n_g, chunk);
-    const int tw_n = ch.toks[n], tw_y0 = ch.toks[yr], tw_y1 = ch.toks[yr + 8];  // with the header
-    Item it;
-    int cnt;
-    if (!chunk_header(rec, T, S, ch, it, cnt)) continue;
-    auto tok = [&](int q, int t) { return q < cnt ? (t < 0 ? 0 : (t >= T ? T - 1 : t)) : -1; };
-    const int tok_n = tok(n, tw_n), ytok0 = tok(yr, tw_y0), ytok1 = tok(yr + 8, tw_y1);
-    const int s = __builtin_amdgcn_readfirstlane(it.slot);
+    int s, cnt, tok_n, ytok0, ytok1;
+    if constexpr (FROM_IDX) {
+      idx_chunk(chunk, s, cnt);
+      tok_n = s_tok[n];
+      ytok0 = s_tok[yr];
+      ytok1 = s_tok[yr + 8];
+    } else {
+      const Chunk ch = chunk_at(rec, T, S, n_g, chunk);
+      const int tw_n = ch.toks[n], tw_y0 = ch.toks[yr], tw_y1 = ch.toks[yr + 8];  // with the header
+      Item it;
+      if (!chunk_header(rec, T, S, ch, it, cnt)) continue;
+      auto tok = [&](int q, int t) { return q < cnt ? (t < 0 ? 0 : (t >= T ? T - 1 : t)) : -1; };
+      tok_n = tok(n, tw_n);
+      ytok0 = tok(yr, tw_y0);
+      ytok1 = tok(yr + 8, tw_y1);
+      s = __builtin_amdgcn_readfirstlane(it.slot);
+    }
     const int r = __builtin_amdgcn_readfirstlane(slot_rank(e.ranks, s, r_max));
     const bool write_v = f.v_out && ct_begin == 0 && wave == 0;
     float* vrow = f.v_out ? f.v_out + (int64_t)sl * p.v_slice_stride + (int64_t)(tok_n >= 0 ? tok_n : 0) * r_max
@@ -274,12 +430,12 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   }
 }
 
-template <typename Elem>
+template <typename Elem, bool FROM_IDX>
 hipError_t fused_launch(const FusedParams& f, hipStream_t stream) {
-  const void* kernel = reinterpret_cast<const void*>(&fused_kernel<Elem>);
+  const void* kernel = reinterpret_cast<const void*>(&fused_kernel<Elem, FROM_IDX>);
   // the grid is what the chip holds at once: consumers wait for producers
   const int grid = persistent_grid(kernel, kFThreads, 0, INT64_MAX / 4);
-  hipLaunchKernelGGL(fused_kernel<Elem>, dim3(grid), dim3(kFThreads), 0, stream, f);
+  hipLaunchKernelGGL((fused_kernel<Elem, FROM_IDX>), dim3(grid), dim3(kFThreads), 0, stream, f);
   return hipGetLastError();
 }
 
@@ -306,7 +462,7 @@ FusedLayout fused_layout(int64_t bytes) {
   return W;
 }
 
-hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, char* ws,
+hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, const int32_t* idx, char* ws,
                         int64_t ws_bytes, float* v_out, hipStream_t stream) {
   const FusedLayout W = fused_layout(ws_bytes);
   FusedParams f;
@@ -316,9 +472,11 @@ hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParam
   f.counters = reinterpret_cast<int32_t*>(ws + W.counters);
   f.err = reinterpret_cast<int32_t*>(ws);
   f.v_out = v_out;
+  f.idx = idx;
+  const bool from_idx = idx != nullptr;
   switch (dt) {
-    case LORA_F16: return fused_launch<half_t>(f, stream);
-    case LORA_BF16: return fused_launch<bf16_t>(f, stream);
+    case LORA_F16: return from_idx ? fused_launch<half_t, true>(f, stream) : fused_launch<half_t, false>(f, stream);
+    case LORA_BF16: return from_idx ? fused_launch<bf16_t, true>(f, stream) : fused_launch<bf16_t, false>(f, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -214,6 +214,12 @@ lora_status lora_expand(lora_dtype dt, const float *v, int64_t v_slice_stride, i
  *   B, out_sizes, out_offsets    as lora_expand; y, ldy as lora_expand
  *   v          nullable; [n_slices][T][r_max] fp32 device.  When given it is
  *              written in full, exactly as lora_shrink writes it.
+ *   idx        nullable; the batch's [T] int32 slots (those the record is
+ *              built from).  When given and the call runs as one launch (see
+ *              below), every workgroup groups the tokens by slot itself, in
+ *              LDS, and seg is not read: the first LoRA layer of a batch can
+ *              then run while lora_build_segments builds the record for the
+ *              later layers on another stream.  Otherwise seg is read.
  *   workspace  device memory of workspace_bytes >=
  *              lora_shrink_expand_workspace_bytes(T, S, n_slices, r_max)
  *              bytes, 256-byte aligned, owned by the caller; pass the same
@@ -243,9 +249,9 @@ lora_status lora_shrink_expand(lora_dtype dt, const void *x, int64_t ldx, int32_
                                int32_t n_slices, const void *const *A, const void *const *B,
                                const int64_t *out_sizes, const int64_t *out_offsets, int32_t S,
                                int32_t r_max, const int32_t *ranks, const float *scale,
-                               const void *seg, int32_t active_hint, float *v, void *y,
-                               int64_t ldy, void *workspace, size_t workspace_bytes,
-                               hipStream_t stream);
+                               const void *seg, const int32_t *idx, int32_t active_hint,
+                               float *v, void *y, int64_t ldy, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                              */

@@ -44,13 +44,16 @@ def fused_counter_bytes(ws):
     return 256 + ws.numel() // 4
 
 
-def run_fused(p, d, seg, ws=None):
-    """shrink_expand on device tensors d; checks the workspace is left clean."""
+def run_fused(p, d, seg, ws=None, from_idx=False):
+    """shrink_expand on device tensors d; checks the workspace is left clean.
+    from_idx: pass the batch's idx, so that a one-launch call groups the
+    tokens itself instead of reading the record."""
     v = torch.full((p.n_slices, p.T, p.r_max), float("nan"), dtype=torch.float32, device=d["x"].device)
     if ws is None:
         ws = glsa.alloc_workspace(p.T, p.S, p.n_slices, p.r_max, d["x"].device)
     glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], seg, p.out_offsets, workspace=ws,
-                       scale=d["scale"], ranks=d["ranks"], v=v)
+                       scale=d["scale"], ranks=d["ranks"], v=v,
+                       idx=d["idx"] if from_idx else None)
     torch.cuda.synchronize()
     assert glsa.workspace_errors(ws) == 0, "a fused wait gave up"
     if p.dtype != "f32" and p.T > 0:
@@ -59,11 +62,13 @@ def run_fused(p, d, seg, ws=None):
 
 
 def run_gpu(p, *, mode="auto", device="cuda", shared_v=False, fused=False):
-    """Build segments, shrink and expand on the GPU.  Returns (v, y, info)."""
+    """Build segments, shrink and expand on the GPU.  Returns (v, y, info).
+    fused: False, "record" (shrink_expand reading the record) or "idx"
+    (shrink_expand grouping the tokens itself where it runs as one launch)."""
     d = problem_to_device(p, device)
     seg = glsa.build_segments(d["idx"], p.S, mode=mode)
     if fused:
-        v = run_fused(p, d, seg)
+        v = run_fused(p, d, seg, from_idx=fused == "idx")
     elif shared_v:
         v = glsa.shrink(d["x"], d["A"][:1], seg, scale=d["scale"], ranks=d["ranks"])
         glsa.expand(v, d["B"], d["y"], seg, p.out_offsets, ranks=d["ranks"], v_slice_stride=0)

@@ -173,7 +173,7 @@ def test_python_binding_raises_lora_error():
 
 def _fused(**kw):
     a = dict(dt=1, x=FAKE, ldx=64, T=8, D=64, n_slices=1, A=[FAKE], B=[FAKE], sizes=[64],
-             offs=[0], S=4, r_max=16, ranks=None, scale=None, seg=FAKE, active=1, v=None,
+             offs=[0], S=4, r_max=16, ranks=None, scale=None, seg=FAKE, idx=None, active=1, v=None,
              y=FAKE, ldy=64, ws=FAKE, ws_bytes=None)
     a.update(kw)
     n = a["n_slices"]
@@ -185,7 +185,7 @@ def _fused(**kw):
     offs = (ctypes.c_int64 * len(a["offs"]))(*a["offs"])
     return glsa.lib().lora_shrink_expand(a["dt"], a["x"], a["ldx"], a["T"], a["D"], n, A, B, sizes,
                                          offs, a["S"], a["r_max"], a["ranks"], a["scale"], a["seg"],
-                                         a["active"], a["v"], a["y"], a["ldy"], a["ws"],
+                                         a["idx"], a["active"], a["v"], a["y"], a["ldy"], a["ws"],
                                          a["ws_bytes"], None)
 
 

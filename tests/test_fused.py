@@ -1,8 +1,10 @@
 """GPU: the one-call shrink_expand (one launch for 16-bit data) matches the fp64
 oracle to the same bars as shrink followed by expand, on the five workloads
-and the edge cases; it leaves its workspace's counters at zero after every
+and the edge cases, both reading the segment record and grouping the tokens
+itself from idx; it leaves its workspace's counters at zero after every
 call, so one workspace serves calls in stream order on batches of any shape;
-and a captured step with it replays correctly."""
+and a captured step with it (the record built on a side stream while the
+first layer runs) replays correctly."""
 
 import numpy as np
 import pytest
@@ -22,16 +24,18 @@ FULL = [("tiny_bgmv", None), ("decode_qproj", None), ("prefill_qkv", 256),
         ("mixed_rank_mlp", None), ("zipf_many", 512)]
 
 
+@pytest.mark.parametrize("source", ["record", "idx"])
 @pytest.mark.parametrize("name,n_sample", FULL, ids=[f[0] for f in FULL])
-def test_fused_workload_parity(name, n_sample):
+def test_fused_workload_parity(name, n_sample, source):
     wl = make_workload(name)
     for p in wl.problems:
         tokens = None if n_sample is None else sample_tokens(p.idx, p.S, n_sample)
-        check_problem(p, tokens=tokens, fused=True, label=f"fused/{name}/{p.name}")
+        check_problem(p, tokens=tokens, fused=source, label=f"fused-{source}/{name}/{p.name}")
 
 
+@pytest.mark.parametrize("source", ["record", "idx"])
 @pytest.mark.parametrize("case", list(edge_problems()), ids=lambda c: c[0])
-def test_fused_edge_parity(case):
+def test_fused_edge_parity(case, source):
     label, p, mode = case
     if p.ranks is not None:  # garbage in the rank padding must be ignored
         for s, r in enumerate(p.ranks):
@@ -39,7 +43,30 @@ def test_fused_edge_parity(case):
                 a[s, r:, :] = a.dtype.type(7) if a.dtype != np.uint16 else np.uint16(0x40e0)
             for b in p.B:
                 b[s, :, r:] = b.dtype.type(7) if b.dtype != np.uint16 else np.uint16(0x40e0)
-    check_problem(p, mode=mode, fused=True, label=f"fused/{label}")
+    check_problem(p, mode=mode, fused=source, label=f"fused-{source}/{label}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fused_idx_mode_does_not_read_the_record(dtype):
+    """With idx given, a one-launch call groups the tokens itself: a record
+    full of garbage (as if still being built on another stream) changes
+    nothing.  Covers every slot count up to 16 tokens per chunk, a slot past
+    64 tokens, base-only and out-of-range tokens."""
+    rng = np.random.default_rng(31)
+    idx = np.concatenate([np.full(70, 2), rng.integers(-3, 12, 300), np.arange(10)]).astype(np.int32)
+    rng.shuffle(idx)
+    p = random_problem(rng, T=idx.size, D=320, out_sizes=(96, 256), r_max=32, S=10, dtype=dtype,
+                       idx=idx, with_ranks=True)
+    d = problem_to_device(p, "cuda")
+    seg = glsa.alloc_segments(p.T, p.S, "cuda")
+    seg.fill_(-7)
+    v = run_fused(p, d, seg, from_idx=True)
+    v_ref, y_ref = oracle_ref(p)
+    y = oracle.decode(from_torch(d["y"], p.dtype), p.dtype)
+    assert rel_err(y, y_ref) <= Y_TOL[p.dtype]
+    assert rel_err(v.cpu().numpy(), v_ref) <= V_TOL
+    valid = (p.idx >= 0) & (p.idx < p.S)
+    assert np.array_equal(from_torch(d["y"], p.dtype)[~valid], p.y_in[~valid])
 
 
 def test_fused_workspace_reuse_across_batches():
@@ -61,7 +88,7 @@ def test_fused_workspace_reuse_across_batches():
             say(f"[fused reuse] round {rnd} problem {i} T={p.T} slices={p.out_sizes} r_max={p.r_max}")
             d = problem_to_device(p, "cuda")
             seg = glsa.build_segments(d["idx"], p.S)
-            v = run_fused(p, d, seg, ws=ws)
+            v = run_fused(p, d, seg, ws=ws, from_idx=(i + rnd) % 2 == 1)
             v_ref, y_ref = oracle_ref(p)
             y = oracle.decode(from_torch(d["y"], p.dtype), p.dtype)
             assert rel_err(y, y_ref) <= Y_TOL[p.dtype]
@@ -95,11 +122,22 @@ def test_fused_graph_replays(name):
     wss = [glsa.alloc_workspace(p.T, p.S, p.n_slices, p.r_max, "cuda") for p in probs]
     y_in = [d["y"].clone() for d in ds]
 
+    side = torch.cuda.Stream()
+
     def step():
-        glsa.build_segments(ds[0]["idx"], wl.S, seg=seg)
-        for p, d, v, ws in zip(probs, ds, vs, wss):
+        # the record is built on a side stream while the first layer groups
+        # the tokens itself; later layers read the record after the join
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            glsa.build_segments(ds[0]["idx"], wl.S, seg=seg)
+        for li, (p, d, v, ws) in enumerate(zip(probs, ds, vs, wss)):
+            if li == 1:
+                main.wait_stream(side)
             glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], seg, p.out_offsets, workspace=ws,
-                               scale=d["scale"], ranks=d["ranks"], v=v)
+                               scale=d["scale"], ranks=d["ranks"], v=v,
+                               idx=d["idx"] if li == 0 else None)
+        main.wait_stream(side)
 
     def reset():
         for d, y0 in zip(ds, y_in):
