@@ -83,7 +83,8 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
       }
   };
   // A operand: this wave's 64 B rows of column tile `ct` (4 blocks x 16), both
-  // rank steps; rank columns past the slot's rank are not read
+  // rank steps; rank columns past the slot's rank are not read (zeros past
+  // ct_end: the last prefetch issues only loads of the zero constant)
   auto load_b = [&](int ct, u32x4 (&bop)[4][2]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
 #pragma unroll
@@ -92,7 +93,7 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int k0 = ks * 32 + kg * 8;
-        const bool ok = ks < nks && row < out && k0 < r;
+        const bool ok = ct < ct_end && ks < nks && row < out && k0 < r;
         bop[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok);
       }
     }
@@ -142,14 +143,10 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
   }
   lds_barrier();  // the v operands are visible; y and B loads stay in flight
 
-  for (int ct = ct_begin; ct < ct_end; ++ct) {
+  // one column tile with its y and B rows (loaded one tile ahead)
+  auto compute_tile = [&](int ct, const u32x4 (&ycur)[NSUB][2], const u32x4 (&bcur)[4][2]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
     const bool ycol_ok = jw + yc < out;  // out is a multiple of 8
-    // B rows are requested before the next tile's y, so that waiting for them
-    // never waits for that prefetch (loads complete in order)
-    if (ct > ct_begin) load_b(ct, bop);
-    u32x4 ynext[NSUB][2];
-    load_y(ct + 1, ynext);
     // a rank that is not a multiple of 8 ends inside one 16-byte piece: zero
     // the columns past it (loaded pieces past the rank are zeros already)
     V bv[4][2];
@@ -157,7 +154,7 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        bv[cb][ks] = as_vec<V>(ragged_rank ? mask_tail16(bop[cb][ks], ks * 32 + kg * 8, r) : bop[cb][ks]);
+        bv[cb][ks] = as_vec<V>(ragged_rank ? mask_tail16(bcur[cb][ks], ks * 32 + kg * 8, r) : bcur[cb][ks]);
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
       if (sb >= n_sub) break;
@@ -196,7 +193,7 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
           u32x4 o;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const uint32_t wd = yold[sb][h][q];
+            const uint32_t wd = ycur[sb][h][q];
             const float y0 = Tr::elem_to_float(wd & 0xffffu) + add[2 * q];
             const float y1 = Tr::elem_to_float(wd >> 16) + add[2 * q + 1];
             if constexpr (Tr::kDtype == LORA_BF16) o[q] = pack2_bf16(y0, y1);
@@ -211,11 +208,19 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-#pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) {
-      yold[sb][0] = ynext[sb][0];
-      yold[sb][1] = ynext[sb][1];
-    }
+  };
+
+  // two tiles per iteration, so that the register buffers alternate without
+  // copies; the next tile's y and B rows are in flight during each tile
+  u32x4 ynext[NSUB][2], bnext[4][2];
+  for (int ct = ct_begin; ct < ct_end; ct += 2) {
+    load_y(ct + 1, ynext);
+    load_b(ct + 1, bnext);
+    compute_tile(ct, yold, bop);
+    if (ct + 1 >= ct_end) break;
+    load_y(ct + 2, yold);
+    load_b(ct + 2, bop);
+    compute_tile(ct + 1, ynext, bnext);
   }
 }
 
