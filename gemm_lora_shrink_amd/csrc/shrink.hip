@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kThreads = kUnitThreads;
 constexpr int kZeroRows = 64;  // tail entries per zero unit
-constexpr int kRingBytes = 32768;  // LDS ring of one wave (also holds its partial sums)
+constexpr int kRingBytes = 16384;  // LDS ring of one wave (also holds its partial sums)
 
 // Token / rank pieces and K parts of every item of a list.
 struct Split {
@@ -48,7 +48,7 @@ struct Split {
 // added with atomics; otherwise zero units clear the rows of tokens without
 // an adapter.
 template <typename Elem>
-__global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int use_tiles, int use_groups,
+__global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int use_tiles, int use_groups,
                                                             int resident, int cleared) {
   __shared__ __attribute__((aligned(1024))) char s_lds[kWaves * kRingBytes];
   __shared__ int s_tok[kTile];
@@ -188,12 +188,14 @@ __global__ __launch_bounds__(kThreads, 1) void shrink_kernel(ShrinkParams p, int
 template <typename Elem>
 hipError_t launch(const ShrinkParams& p, bool groups, bool tiles, hipStream_t stream) {
   const void* kernel = reinterpret_cast<const void*>(&shrink_kernel<Elem>);
-  // The kernel is persistent, aiming at about three quarters of the
-  // workgroups the chip holds at once.  When even a batch of nothing but full
-  // tiles, with every piece cut, would give fewer units, items may also be
-  // cut along K: v is cleared first.
+  // The kernel is persistent: its grid is the workgroups the chip holds at
+  // once (two per compute unit, each with four 16 KB LDS rings).  When even a
+  // batch of nothing but full tiles, with every piece cut, would give fewer
+  // units than about three quarters of the compute units, items may also be
+  // cut along K: v is cleared first.  (Mid-size batches, which would fill the
+  // compute units once, run faster without the atomics.)
   const int resident = persistent_grid(kernel, kThreads, 0, INT64_MAX / 4);
-  const bool cleared = ceil_div(p.T, kTile) * p.n_slices * (kTile / 16) * ceil_div(p.r_max, 16) < resident * 3 / 4;
+  const bool cleared = ceil_div(p.T, kTile) * p.n_slices * (kTile / 16) * ceil_div(p.r_max, 16) < resident * 3 / 8;
   if (cleared) {
     hipError_t e = launch_fill_zero(p.v, (int64_t)p.n_slices * p.v_slice_stride, stream);
     if (e != hipSuccess) return e;
