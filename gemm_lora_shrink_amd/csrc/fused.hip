@@ -47,7 +47,7 @@ namespace {
 
 constexpr int kFThreads = kUnitThreads;
 constexpr int kFRing = 16384;        // per-wave LDS ring: 64 KB per workgroup, two workgroups per CU
-constexpr int kMaxParts = 8;         // K parts per chunk
+constexpr int kMaxParts = 4;         // K parts per chunk
 constexpr int kFusedUnits = 1024;    // at most this many producer slabs when chunks are cut into K parts
 constexpr int kSpinLimit = 1 << 20;  // polls (about a microsecond each) before a wait gives up
 constexpr int kZeroRowsF = 64;       // tail entries per zero unit
