@@ -4,8 +4,8 @@
 // compilation", review of the token index buffer); every LoRA layer of the
 // batch then reuses this record.
 //
-// One workgroup of 1024 threads (16 waves) does everything, so the result is
-// bit-exact and deterministic.  Wave w owns the contiguous token range
+// One workgroup (16 waves; 4 for batches of at most 1024 tokens and 256
+// slots) does everything, so the result is bit-exact and deterministic.  Wave w owns the contiguous token range
 // [w R, (w + 1) R), walked in chunks of 64 (one token per lane).  The key of a
 // token is its slot, or S for a token without a valid slot (those follow every
 // active token in perm, ascending, and the shrink clears their v rows).
@@ -34,8 +34,13 @@ namespace lora {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
+// The kernel is one workgroup of NT threads: 1024 in general, 256 for small
+// batches (T <= kSmallT, S <= 256), where fewer waves mean shorter per-key
+// table walks and cheaper barriers.  A slot is owned by thread `slot` in the
+// scan, so S <= NT.
+constexpr int kThreadsLarge = 1024;
+constexpr int kThreadsSmall = 256;
+constexpr int kSmallT = 1024;
 constexpr int kRegChunks = 8;   // chunks per wave kept in registers
 constexpr int kLdsPerm = 8192;  // perm positions mirrored in LDS
 constexpr int kItemTab = 2048;  // items whose slot is tabulated in LDS
@@ -98,6 +103,7 @@ __device__ inline int wave_max_nonneg(int v) {
 // Block-wide exclusive scan of four ints per thread (thread order), returning
 // the exclusive prefixes and writing the four totals to `total`.  Only threads
 // below S hold nonzero values; with S <= 64 one wave's scan is the whole scan.
+template <int kWaves>
 __device__ inline void block_exclusive_scan4(int4& v, int4* wave_sums, int4& total, int S) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -143,8 +149,10 @@ __device__ inline int upper_slot(const int* arr, int n, int key) {
   return lo;
 }
 
+template <int kThreads>
 __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t* __restrict__ idx, int T, int S,
                                                                   int mode, int32_t* __restrict__ rec) {
+  constexpr int kWaves = kThreads / 64;
   __shared__ int s_tab[kWaves][LORA_MAX_SLOTS + 1];  // per-(wave, key) counts, then run starts
   __shared__ int s_count[LORA_MAX_SLOTS];
   __shared__ int s_start[LORA_MAX_SLOTS];
@@ -248,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
   }
   int4 sc = make_int4(n_slot, n_slot > 0 ? 1 : 0, ng, nt);
   int4 tot;
-  block_exclusive_scan4(sc, s_wave_sums, tot, S);
+  block_exclusive_scan4<kWaves>(sc, s_wave_sums, tot, S);
   const int num_active = tot.x, num_seg = tot.y, n_groups = tot.z, n_tiles = tot.w;
   // keys 0 .. S (key S, the tokens without a slot, starts after every active
   // token; with S = 1024 thread 0 also takes it)
@@ -362,7 +370,12 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t*
 
 hipError_t launch_build_segments(const int32_t* idx, int32_t T, int32_t S, int32_t mode, int32_t* rec,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(kThreads), 0, stream, idx, T, S, mode, rec);
+  if (T <= kSmallT && S <= kThreadsSmall)
+    hipLaunchKernelGGL(build_segments_kernel<kThreadsSmall>, dim3(1), dim3(kThreadsSmall), 0, stream, idx, T, S,
+                       mode, rec);
+  else
+    hipLaunchKernelGGL(build_segments_kernel<kThreadsLarge>, dim3(1), dim3(kThreadsLarge), 0, stream, idx, T, S,
+                       mode, rec);
   return hipGetLastError();
 }
 

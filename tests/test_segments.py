@@ -85,6 +85,13 @@ def edge_cases():
     yield "descending", np.repeat(np.arange(30, -1, -1, dtype=np.int32), 70), 31
     z = rng.choice(200, size=6000, p=(np.arange(200) + 1.0) ** -1.3 / np.sum((np.arange(200) + 1.0) ** -1.3))
     yield "zipf_200", z.astype(np.int32), 200
+    # around the switch between the 4-wave build (T <= 1024, S <= 256) and the
+    # 16-wave one: largest small batch, one token more, one slot more
+    yield "small_T1024_S256", rng.integers(-1, 256, size=1024).astype(np.int32), 256
+    yield "large_T1025_S256", rng.integers(-1, 256, size=1025).astype(np.int32), 256
+    yield "large_T1024_S257", rng.integers(-1, 257, size=1024).astype(np.int32), 257
+    yield "small_one_slot_full", np.zeros(1024, np.int32), 1
+    yield "small_wave_edges", np.repeat(np.arange(4, dtype=np.int32), [255, 257, 1, 511]), 4
 
 
 @pytest.mark.parametrize("case", list(edge_cases()), ids=lambda c: c[0])
