@@ -19,7 +19,8 @@ its algorithmic bytes (active rows, distinct slots at their real ranks, the
 fp32 intermediate's write and read) divided by its average duration, measured
 here with HIP events around graph replays of that call alone.  `cpu_baseline`
 is the fp64 oracle timed on a bounded sample of the same workload on the
-host cores.
+host cores.  For an all-base batch (zipf_many_noop) a `noop` object times the
+layer's base projection with and without the (no-op) LoRA call.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -169,6 +170,58 @@ def cpu_baseline(wl, seconds):
 # --------------------------------------------------------------------------
 # GPU side
 # --------------------------------------------------------------------------
+
+def noop_overhead(torch, glsa, st, p, S, capture, reps=20, iters=50):
+    """The cost of the LoRA path on an all-base batch, next to the base layer.
+
+    The base layer is the layer's own dense projection, y = x W^T (a
+    T x D by D x out fp16 GEMM, as the q_proj of Llama-3-8B at T = 4096).  With
+    LoRA enabled and no adapter active the caller passes active = False (the
+    host knows the batch holds no adapter) and shrink_expand enqueues nothing.
+    Both loops are timed in graph replay and eager, `iters` layers per timing,
+    median of `reps`; overhead = with_lora / base - 1.
+    """
+    import statistics
+    d = st["layers"][0]
+    x = d["x"]
+    W = torch.randn((sum(p.out_sizes), p.D), device=x.device, dtype=x.dtype) * 0.01
+    out = torch.empty((x.size(0), W.size(0)), device=x.device, dtype=x.dtype)
+
+    def base():
+        torch.matmul(x, W.t(), out=out)
+
+    def with_lora():
+        torch.matmul(x, W.t(), out=out)
+        glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], st["seg"], p.out_offsets,
+                           workspace=d["ws"], scale=d["scale"], ranks=d["ranks"], v=d["v"],
+                           active=False)
+
+    def timed(fn_iter):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        vals = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0.record()
+            fn_iter()
+            e1.record()
+            torch.cuda.synchronize()
+            vals.append(e0.elapsed_time(e1) * 1e3 / iters)
+        return statistics.median(vals)
+
+    res = {}
+    for mode in ("graph", "eager"):
+        t = {}
+        for name, fn in (("base", base), ("with_lora", with_lora)):
+            if mode == "graph":
+                g = capture([fn] * iters)
+                t[name] = timed(g.replay)
+            else:
+                t[name] = timed(lambda fn=fn: [fn() for _ in range(iters)])
+        res[mode] = dict(base_us=round(t["base"], 3), with_lora_us=round(t["with_lora"], 3),
+                         overhead=round(t["with_lora"] / t["base"] - 1.0, 5))
+    res["base_layer"] = f"fp16 GEMM [{x.size(0)} x {p.D}] x [{p.D} x {W.size(0)}] (torch.matmul)"
+    return res
+
 
 def main():
     args = parse()
@@ -379,6 +432,10 @@ def main():
                     alg_bytes_per_launch=dom["bytes"], avg_launch_us=round(dom["us"], 3),
                     source_hash=kernel_source_hash())
 
+    noop = None
+    if not active:
+        noop = noop_overhead(torch, glsa, sets[0], problems[0], S, capture)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(wl, args.cpu_seconds)
@@ -404,6 +461,8 @@ def main():
         roofline=roofline,
         cpu_baseline=cpu,
     )
+    if noop is not None:
+        out["noop"] = noop
     line = json.dumps(out)
     print(line, flush=True)
     if args.json_out:
