@@ -37,6 +37,8 @@
 // depends only on its size (counters in its first quarter, after a 256-byte
 // header), so calls of any shape on one workspace use the same counter region
 // and never write their slabs over another call's counters.
+#include <stdlib.h>
+
 #include "common.h"
 #include "expand_unit.h"
 #include "shrink_unit.h"
@@ -61,6 +63,7 @@ struct FusedParams {
   int32_t* err;       // waits that gave up
   float* v_out;       // nullable: v written in full when given
   const int32_t* idx; // the batch's slots: grouped in each workgroup (idx mode)
+  int spin_limit;     // polls before a wait gives up
 };
 
 // idx mode: every workgroup groups the batch's tokens by slot itself, in LDS,
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       if (tid == 0) {
         int spins = 0;
         while (__hip_atomic_load(cnt_ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-          if (++spins > kSpinLimit) {
+          if (++spins > f.spin_limit) {
             atomicAdd(f.err, 1);
             break;
           }
@@ -473,6 +476,13 @@ hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParam
   f.err = reinterpret_cast<int32_t*>(ws);
   f.v_out = v_out;
   f.idx = idx;
+  // LORA_MI355X_FUSED_SPIN_LIMIT (a count of polls >= 0) replaces the bound on
+  // the consumers' waits, so that tests can force the give-up path from the host
+  f.spin_limit = kSpinLimit;
+  if (const char* e = getenv("LORA_MI355X_FUSED_SPIN_LIMIT")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= 0 && v < kSpinLimit) f.spin_limit = (int)v;
+  }
   const bool from_idx = idx != nullptr;
   switch (dt) {
     case LORA_F16: return from_idx ? fused_launch<half_t, true>(f, stream) : fused_launch<half_t, false>(f, stream);

@@ -231,7 +231,10 @@ lora_status lora_expand(lora_dtype dt, const float *v, int64_t v_slice_stride, i
  *              overlap (other streams) need distinct workspaces.  int32 word 0
  *              counts device-side waits that gave up (0 in every normal run;
  *              if it is not 0 the call's output is invalid and the workspace
- *              must be cleared again).
+ *              must be cleared again).  Each wait gives up after a bounded
+ *              number of polls, so a call always ends; the environment
+ *              variable LORA_MI355X_FUSED_SPIN_LIMIT, when set, lowers that
+ *              bound (for tests of the give-up path).
  * fp16/bf16 batches of T <= lora_fused_max_tokens() run as one launch:
  * producer work units shrink 16-token chunks over ranges of D into the
  * workspace and consumer units expand each chunk once every part of it is

@@ -178,3 +178,34 @@ def test_fused_graph_replays(name):
             v_ref, y_ref = refs[li]
             assert rel_err(vg[:, rows], v_ref) <= V_TOL
             assert rel_err(yg[rows], y_ref) <= Y_TOL[p.dtype]
+
+
+def test_fused_wait_give_up_is_bounded_and_recoverable(monkeypatch):
+    """Forced from the host: with at most one poll per wait, consumers that
+    find their chunk incomplete give up at once.  The call still ends; either
+    every wait succeeded (and y is right) or the give-ups are counted in the
+    workspace.  After the workspace is cleared, as the header prescribes, the
+    next call is right again."""
+    wl = make_workload("decode_qproj")
+    p = wl.problems[0]
+    d = problem_to_device(p, "cuda")
+    seg = glsa.build_segments(d["idx"], p.S)
+    ws = glsa.alloc_workspace(p.T, p.S, p.n_slices, p.r_max, "cuda")
+    y0 = d["y"].clone()
+    _, y_ref = oracle_ref(p)
+    monkeypatch.setenv("LORA_MI355X_FUSED_SPIN_LIMIT", "0")
+    glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], seg, p.out_offsets, workspace=ws,
+                       scale=d["scale"], ranks=d["ranks"])
+    torch.cuda.synchronize()  # returns: every wave exited
+    gave_up = glsa.workspace_errors(ws)
+    err = rel_err(oracle.decode(from_torch(d["y"], p.dtype), p.dtype), y_ref)
+    say(f"[fused give-up] waits given up {gave_up}, y error {err:.2e}")
+    assert gave_up > 0 or err <= Y_TOL[p.dtype]
+    monkeypatch.delenv("LORA_MI355X_FUSED_SPIN_LIMIT")
+    ws.zero_()
+    d["y"].copy_(y0)
+    glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], seg, p.out_offsets, workspace=ws,
+                       scale=d["scale"], ranks=d["ranks"])
+    torch.cuda.synchronize()
+    assert glsa.workspace_errors(ws) == 0
+    assert rel_err(oracle.decode(from_torch(d["y"], p.dtype), p.dtype), y_ref) <= Y_TOL[p.dtype]
