@@ -3,10 +3,12 @@
 
 A step is one pass of the whole path over one batch: the segment build, then
 for every LoRA layer of the workload its shrink and (where timed) its expand.
-By default each layer with a timed expand is one shrink_expand call.  With
---overlap the first such call groups the tokens itself and the segment record
-(which the later layers read) is built beside it on a second stream, inside
-the same step.
+By default each layer with a timed expand is one shrink_expand call, and the
+first one is given the batch's idx so that it builds the segment record
+itself (inside its single launch for 16-bit batches of at most 2048 tokens
+and 256 slots); the later layers read that record.  --separate-build runs
+lora_build_segments first instead.  The segment build is timed on its own as
+the `segments` call either way.
 Inputs are resident in HBM before timing starts.  Steps rotate over several
 device copies of the inputs, enough that the working set exceeds the 256 MB
 last-level cache, so the byte rates below are HBM rates, not cache rates.
@@ -49,9 +51,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", default="auto", choices=["auto", "bgmv", "sgmv"])
-    ap.add_argument("--overlap", action="store_true",
-                    help="build the segment record on a second stream beside the first layer, which "
-                         "then groups the tokens itself (measured slower on MI355X: off by default)")
+    ap.add_argument("--separate-build", action="store_true",
+                    help="build the segment record with lora_build_segments before the first layer "
+                         "instead of inside the first layer's shrink_expand call")
     ap.add_argument("--eager", action="store_true", help="time host launches instead of graph replay")
     ap.add_argument("--path", default="fused", choices=["fused", "split"],
                     help="fused: each layer with a timed expand is one shrink_expand call (one "
@@ -289,39 +291,28 @@ def main():
                     active=active)
 
     fused = args.path == "fused"
-    # The first layer of a batch needs no segment record when its shrink_expand
-    # runs as one launch and groups the tokens itself from idx: the record for
-    # the later layers is then built on a side stream at the same time.
-    overlap = (fused and args.overlap and problems[0].timed_expand
-               and wl.dtype in ("f16", "bf16") and T <= glsa.fused_max_tokens())
+    # The first layer's shrink_expand call builds the segment record itself
+    # when given idx (inside its one launch for 16-bit batches of at most
+    # lora_fused_max_tokens() tokens and 256 slots); the later layers read it.
+    build_in_call = (fused and not args.separate_build and active and problems[0].timed_expand
+                     and wl.dtype in ("f16", "bf16") and T <= glsa.fused_max_tokens() and S <= 256)
 
     def do_fused(st, li):
         d, p = st["layers"][li], problems[li]
         glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], st["seg"], p.out_offsets,
                            workspace=d["ws"], scale=d["scale"], ranks=d["ranks"], v=d["v"],
-                           idx=st["idx"] if overlap and li == 0 else None, active=active)
-
-    side = torch.cuda.Stream()
+                           idx=st["idx"] if build_in_call and li == 0 else None, active=active)
 
     def step(st):
-        main = torch.cuda.current_stream()
-        if overlap:
-            side.wait_stream(main)
-            with torch.cuda.stream(side):
-                do_segments(st)
-        else:
+        if not build_in_call:
             do_segments(st)
         for li, p in enumerate(problems):
-            if overlap and li == 1:
-                main.wait_stream(side)  # later layers read the record
             if fused and p.timed_expand:
                 do_fused(st, li)
                 continue
             do_shrink(st, li)
             if p.timed_expand:
                 do_expand(st, li)
-        if overlap:
-            main.wait_stream(side)
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
@@ -407,9 +398,11 @@ def main():
     if active:
         for li, p in enumerate(problems):
             if fused and p.timed_expand:
-                calls[f"{p.name}.shrink_expand"] = dict(
+                name = f"{p.name}.shrink_expand" + ("+segments" if build_in_call and li == 0 else "")
+                calls[name] = dict(
                     us=call_time_us(lambda st, li=li: do_fused(st, li)),
-                    bytes=alg[li]["shrink_bytes"] + alg[li]["expand_bytes"],
+                    bytes=alg[li]["shrink_bytes"] + alg[li]["expand_bytes"]
+                    + (segment_bytes(T, alg[0]["n_active"]) if build_in_call and li == 0 else 0),
                     flops=alg[li]["shrink_flops"] + alg[li]["expand_flops"])
                 continue
             calls[f"{p.name}.shrink"] = dict(us=call_time_us(lambda st, li=li: do_shrink(st, li)),
@@ -423,8 +416,11 @@ def main():
         c["tflops"] = c["flops"] / (c["us"] * 1e-6) / 1e12 if c["us"] > 0 else 0.0
     dom_name = max(calls, key=lambda k: calls[k]["us"])
     dom = calls[dom_name]
-    step_bytes = sum(c["bytes"] for c in calls.values())
-    step_flops = sum(c["flops"] for c in calls.values())
+    # (with the record built inside the first call, the separately timed
+    # segment build is not part of the step)
+    in_step = [c for k, c in calls.items() if not (build_in_call and k == "segments")]
+    step_bytes = sum(c["bytes"] for c in in_step)
+    step_flops = sum(c["flops"] for c in in_step)
 
     roofline = dict(bound="hbm", kernel=dom_name, achieved=round(dom["gbs"], 1), peak=HBM_PEAK_GBS,
                     unit="GB/s", frac=round(dom["gbs"] / HBM_PEAK_GBS, 4),
@@ -449,7 +445,7 @@ def main():
                     layers=[dict(name=p.name, D=p.D, out=list(p.out_sizes),
                                  timed_expand=p.timed_expand) for p in problems],
                     n_active=alg[0]["n_active"], n_distinct_slots=alg[0]["n_distinct"],
-                    mode=args.mode, path=args.path, record_beside_first_layer=overlap,
+                    mode=args.mode, path=args.path, record_built_in_first_call=build_in_call,
                     timing=timed_mode, input_sets=n_sets,
                     accumulate="fp32"),
         step_gbs=round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),

@@ -264,8 +264,9 @@ def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=
     """Shrink then expand in one call; y updated in place.  Returns y.
 
     v (optional, [n_slices, T, r_max] float32) receives the intermediate.
-    idx (optional, int32 [T]): when given, a one-launch call groups the tokens
-    itself and does not read seg.
+    idx (optional, int32 [T]): when given, the call builds the batch's segment
+    record into seg itself (as build_segments(idx, S) would) before or beside
+    the layer; without it seg must hold the record.
     workspace: from alloc_workspace (zeroed once; every call leaves it reusable).
     """
     A, B = list(A), list(B)

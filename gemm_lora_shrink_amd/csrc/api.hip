@@ -354,14 +354,22 @@ LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t
                    ldy, ep);
   if (st != LORA_OK || T == 0) return st;
   if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
-  hipError_t e;
-  if (dt != LORA_F32 && T <= kFusedMaxTokens) {
+  hipError_t e = hipSuccess;
+  const bool one_launch = dt != LORA_F32 && T <= kFusedMaxTokens;
+  if (one_launch && idx && S <= kFusedBuildMaxSlots) {
+    // the launch builds the record itself, beside the layer
     e = launch_fused(dt, sp, ep, idx, ws, (int64_t)workspace_bytes, v, stream);
   } else {
-    // larger batches stream enough bytes per launch that the launch and the
-    // round trips no longer dominate: the shrink launch then the expand launch
-    e = launch_shrink(dt, sp, /*groups=*/true, /*tiles=*/true, stream);
-    if (e == hipSuccess) e = run_expand(dt, ep, stream);
+    // with idx and no room for the build inside the launch: the build kernel first
+    if (idx) e = launch_build_segments(idx, T, S, LORA_MODE_AUTO, static_cast<int32_t*>(const_cast<void*>(seg)), stream);
+    if (e == hipSuccess && one_launch) {
+      e = launch_fused(dt, sp, ep, nullptr, ws, (int64_t)workspace_bytes, v, stream);
+    } else if (e == hipSuccess) {
+      // larger batches stream enough bytes per launch that the launch and the
+      // round trips no longer dominate: the shrink launch then the expand launch
+      e = launch_shrink(dt, sp, /*groups=*/true, /*tiles=*/true, stream);
+      if (e == hipSuccess) e = run_expand(dt, ep, stream);
+    }
   }
   if (e != hipSuccess) return hip_fail(e, "shrink-expand launch");
   return LORA_OK;

@@ -17,6 +17,7 @@ constexpr int kGroup = 16;  // tokens per gather (BGMV) work item
 constexpr int kTile = 64;   // tokens per segmented (SGMV) work item
 constexpr int kSgmvMinTokens = 48;  // AUTO: slots with this many tokens go to SGMV
 constexpr int kFusedMaxTokens = 2048;  // lora_shrink_expand runs as one launch up to this T
+constexpr int kFusedBuildMaxSlots = 256;  // ... and builds the record inside that launch up to this S
 
 enum InfoWord {
   kNumActive = 0,
@@ -328,7 +329,8 @@ int64_t fused_need_bytes(int64_t T, int64_t S, int64_t n_slices, int64_t r_max);
 // Shrink and expand of the batch's 16-token chunks in one launch (16-bit types
 // only); v_out (nullable) receives v in full.
 // idx (nullable): the batch's slots; when given, the kernel groups the tokens
-// itself (T <= kFusedMaxTokens) and does not read the segment record.
+// itself (T <= kFusedMaxTokens) and one of its workgroups builds the segment
+// record into sp.rec (S <= kFusedBuildMaxSlots); the record is not read.
 hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, const int32_t* idx, char* ws,
                         int64_t ws_bytes, float* v_out, hipStream_t stream);
 

@@ -41,6 +41,7 @@
 
 #include "common.h"
 #include "expand_unit.h"
+#include "segments_block.h"
 #include "shrink_unit.h"
 
 namespace lora {
@@ -64,7 +65,13 @@ struct FusedParams {
   float* v_out;       // nullable: v written in full when given
   const int32_t* idx; // the batch's slots: grouped in each workgroup (idx mode)
   int spin_limit;     // polls before a wait gives up
+  int32_t* rec_out;   // idx mode, nullable: the segment record one workgroup builds
 };
+
+// idx mode also builds the batch's segment record, in one workgroup on this
+// kernel's four waves (so S <= kFThreads), its tables in that workgroup's
+// ring LDS (T <= kFusedMaxTokens positions of perm mirrored).
+using BuildShared = SegShared<kFThreads, kFusedMaxTokens>;
 
 // idx mode: every workgroup groups the batch's tokens by slot itself, in LDS,
 // from idx (T <= kFusedMaxTokens): tokens per slot and the first chunk of each
@@ -231,6 +238,25 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   const int64_t n_z = f.v_out ? ceil_div(FROM_IDX ? T : T - na, kZeroRowsF) * ns : 0;
   const int32_t* perm = rec + seg_layout(T, S).perm;
   const size_t slab_floats = (size_t)16 * r_max;
+
+  // idx mode with a record to build: one workgroup builds it with the block
+  // build of the segment kernel -- the first workgroup with neither producer
+  // nor consumer units, else the last one (which then does its units after)
+  if constexpr (FROM_IDX) {
+    static_assert(sizeof(BuildShared) <= sizeof(s_lds), "the build's tables fit the rings' LDS");
+    if (f.rec_out) {
+      const ExpandParams& eb = f.ep;
+      int64_t pairs = 0;
+      for (int i = 0; i < ns; ++i) pairs += n_chunks * ceil_div(eb.out_size[i], kExpandColsPerWG);
+      const int64_t ge = min(G, max((int64_t)kXcds, ceil_div(pairs, kXcds) * kXcds));
+      const int64_t builder = n_su + n_z < G - ge ? n_su + n_z : G - 1;
+      if (blockIdx.x == builder) {
+        build_segments_block<kFThreads, kFusedMaxTokens>(f.idx, T, S, LORA_MODE_AUTO, f.rec_out,
+                                                         *reinterpret_cast<BuildShared*>(s_lds));
+        __syncthreads();  // the rings' LDS is used again below
+      }
+    }
+  }
 
   // ---- producer units (then zero units) on the first workgroups, which the
   // hardware dispatches first: a producer never waits, so the consumers below
@@ -476,6 +502,7 @@ hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParam
   f.err = reinterpret_cast<int32_t*>(ws);
   f.v_out = v_out;
   f.idx = idx;
+  f.rec_out = idx ? const_cast<int32_t*>(sp.rec) : nullptr;
   // LORA_MI355X_FUSED_SPIN_LIMIT (a count of polls >= 0) replaces the bound on
   // the consumers' waits, so that tests can force the give-up path from the host
   f.spin_limit = kSpinLimit;

@@ -214,12 +214,15 @@ lora_status lora_expand(lora_dtype dt, const float *v, int64_t v_slice_stride, i
  *   B, out_sizes, out_offsets    as lora_expand; y, ldy as lora_expand
  *   v          nullable; [n_slices][T][r_max] fp32 device.  When given it is
  *              written in full, exactly as lora_shrink writes it.
- *   idx        nullable; the batch's [T] int32 slots (those the record is
- *              built from).  When given and the call runs as one launch (see
- *              below), every workgroup groups the tokens by slot itself, in
- *              LDS, and seg is not read: the first LoRA layer of a batch can
- *              then run while lora_build_segments builds the record for the
- *              later layers on another stream.  Otherwise seg is read.
+ *   idx        nullable; the batch's [T] int32 slots.  When given, the call
+ *              builds the batch's segment record into seg itself, exactly as
+ *              lora_build_segments(idx, T, S, LORA_MODE_AUTO, seg) would, and
+ *              ignores what seg held: the first LoRA layer of a batch needs no
+ *              separate build, and the later layers read the record.  When the
+ *              call runs as one launch and S <= 256, every workgroup groups the
+ *              tokens by slot itself, in LDS, and one workgroup builds the
+ *              record beside the layer; otherwise the build kernel runs first.
+ *              Without idx, seg must hold the batch's record.
  *   workspace  device memory of workspace_bytes >=
  *              lora_shrink_expand_workspace_bytes(T, S, n_slices, r_max)
  *              bytes, 256-byte aligned, owned by the caller; pass the same

@@ -3,8 +3,8 @@ oracle to the same bars as shrink followed by expand, on the five workloads
 and the edge cases, both reading the segment record and grouping the tokens
 itself from idx; it leaves its workspace's counters at zero after every
 call, so one workspace serves calls in stream order on batches of any shape;
-and a captured step with it (the record built on a side stream while the
-first layer runs) replays correctly."""
+and a captured step with it (the first layer's call building the record the
+later layers read) replays correctly."""
 
 import numpy as np
 import pytest
@@ -46,21 +46,53 @@ def test_fused_edge_parity(case, source):
     check_problem(p, mode=mode, fused=source, label=f"fused-{source}/{label}")
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_fused_idx_mode_does_not_read_the_record(dtype):
-    """With idx given, a one-launch call groups the tokens itself: a record
-    full of garbage (as if still being built on another stream) changes
-    nothing.  Covers every slot count up to 16 tokens per chunk, a slot past
-    64 tokens, base-only and out-of-range tokens."""
+def _record_words(seg, T, S):
+    """The documented and planned parts of a record (everything the kernels read)."""
+    rec = seg.cpu().numpy()
+    off = {k: glsa.segments_offset(T, S, k) for k in glsa.SEG_FIELDS}
+    info = rec[:16]
+    return np.concatenate([
+        info, rec[off["perm"]:off["perm"] + T],
+        rec[off["seg_slot"]:off["seg_slot"] + info[1]],
+        rec[off["seg_start"]:off["seg_start"] + info[1] + 1],
+        rec[off["groups"]:off["groups"] + 20 * info[4]],
+        rec[off["tiles"]:off["tiles"] + 68 * info[5]]])
+
+
+def _idx_cases():
     rng = np.random.default_rng(31)
     idx = np.concatenate([np.full(70, 2), rng.integers(-3, 12, 300), np.arange(10)]).astype(np.int32)
     rng.shuffle(idx)
-    p = random_problem(rng, T=idx.size, D=320, out_sizes=(96, 256), r_max=32, S=10, dtype=dtype,
-                       idx=idx, with_ranks=True)
+    for dtype in ("f16", "bf16"):
+        # one launch, the record built inside it: a slot past 64 tokens (a
+        # tile), every group size, base-only and out-of-range tokens
+        yield f"in_launch_{dtype}", random_problem(rng, T=idx.size, D=320, out_sizes=(96, 256), r_max=32,
+                                                   S=10, dtype=dtype, idx=idx.copy(), with_ranks=True)
+    # one launch, S past 256: the build kernel runs first
+    yield "build_kernel_S600", random_problem(rng, T=900, D=128, out_sizes=(64,), r_max=16, S=600,
+                                              dtype="f16")
+    # largest one-launch batch with the build inside; then two launches
+    yield "in_launch_T2048", random_problem(rng, T=2048, D=256, out_sizes=(128,), r_max=16, S=256,
+                                            dtype="bf16")
+    yield "two_launches_T2100", random_problem(rng, T=2100, D=256, out_sizes=(128,), r_max=16, S=40,
+                                               dtype="f16")
+    yield "fp32_two_launches", random_problem(rng, T=200, D=64, out_sizes=(32,), r_max=8, S=5,
+                                              dtype="f32", bad_idx_frac=0.1)
+
+
+@pytest.mark.parametrize("case", list(_idx_cases()), ids=lambda c: c[0])
+def test_fused_idx_mode_builds_the_record(case):
+    """With idx given, the call builds the record itself: a record full of
+    garbage beforehand comes out equal, word for word, to the one
+    lora_build_segments builds, and the layer matches the oracle."""
+    label, p = case
     d = problem_to_device(p, "cuda")
+    ref = glsa.build_segments(d["idx"], p.S)  # a separate record, the reference
     seg = glsa.alloc_segments(p.T, p.S, "cuda")
     seg.fill_(-7)
+    say(f"[fused idx] {label} T={p.T} S={p.S} dtype={p.dtype}")
     v = run_fused(p, d, seg, from_idx=True)
+    assert np.array_equal(_record_words(seg, p.T, p.S), _record_words(ref, p.T, p.S)), label
     v_ref, y_ref = oracle_ref(p)
     y = oracle.decode(from_torch(d["y"], p.dtype), p.dtype)
     assert rel_err(y, y_ref) <= Y_TOL[p.dtype]
@@ -111,7 +143,8 @@ def test_fused_inactive_hint_enqueues_nothing():
 
 @pytest.mark.parametrize("name", ["decode_qproj", "mixed_rank_mlp"])
 def test_fused_graph_replays(name):
-    """Segment build + shrink_expand captured once and replayed 4 times, with
+    """shrink_expand layers, the first building the record, captured once and
+    replayed 4 times, with
     the program's own eager work (y reset, v poisoned) and a synchronisation
     between replays; each replay matches the eager run and the oracle."""
     wl = make_workload(name)
@@ -122,28 +155,20 @@ def test_fused_graph_replays(name):
     wss = [glsa.alloc_workspace(p.T, p.S, p.n_slices, p.r_max, "cuda") for p in probs]
     y_in = [d["y"].clone() for d in ds]
 
-    side = torch.cuda.Stream()
-
     def step():
-        # the record is built on a side stream while the first layer groups
-        # the tokens itself; later layers read the record after the join
-        main = torch.cuda.current_stream()
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            glsa.build_segments(ds[0]["idx"], wl.S, seg=seg)
+        # the first layer's call builds the record (idx given); the later
+        # layers read it
         for li, (p, d, v, ws) in enumerate(zip(probs, ds, vs, wss)):
-            if li == 1:
-                main.wait_stream(side)
             glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], seg, p.out_offsets, workspace=ws,
                                scale=d["scale"], ranks=d["ranks"], v=v,
                                idx=d["idx"] if li == 0 else None)
-        main.wait_stream(side)
 
     def reset():
         for d, y0 in zip(ds, y_in):
             d["y"].copy_(y0)
         for v in vs:
             v.fill_(float("nan"))
+        seg.fill_(-7)  # rebuilt by every step
 
     reset()
     step()
