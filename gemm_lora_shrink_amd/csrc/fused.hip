@@ -90,12 +90,7 @@ struct IdxTables {
 // the total.  Every thread calls it.
 __device__ inline int block_exscan(int v, int* scan, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_inclusive_scan(v);  // DPP row shifts and broadcasts, no LDS round trips
   if (lane == 63) scan[wave] = x;
   lds_barrier();
   int before = 0;
