@@ -5,7 +5,7 @@ A step is one pass of the whole path over one batch: the segment build, then
 for every LoRA layer of the workload its shrink and (where timed) its expand.
 By default each layer with a timed expand is one shrink_expand call, and the
 first one is given the batch's idx so that it builds the segment record
-itself (inside its single launch for 16-bit batches of at most 2048 tokens
+itself (inside its single launch for 16-bit batches of at most 4096 tokens
 and 256 slots); the later layers read that record.  --separate-build runs
 lora_build_segments first instead.  The segment build is timed on its own as
 the `segments` call either way.

@@ -70,15 +70,20 @@ struct FusedParams {
 
 // idx mode also builds the batch's segment record, in one workgroup on this
 // kernel's four waves (so S <= kFThreads), its tables in that workgroup's
-// ring LDS (T <= kFusedMaxTokens positions of perm mirrored).
-using BuildShared = SegShared<kFThreads, kFusedMaxTokens>;
+// ring LDS (the batch's T <= TPT x kFThreads positions of perm mirrored).
+template <int TPT>
+using BuildShared = SegShared<kFThreads, TPT * kFThreads>;
 
 // idx mode: every workgroup groups the batch's tokens by slot itself, in LDS,
 // from idx (T <= kFusedMaxTokens): tokens per slot and the first chunk of each
 // slot.  A slot's chunks are its tokens, in token order, cut into runs of 16
 // (the same pieces as the record's gather groups and tile quarters).
-constexpr int kTokPerThread = kFusedMaxTokens / kFThreads;
-static_assert(kTokPerThread * kFThreads == kFusedMaxTokens, "tokens per thread");
+// The kernel's idx form is instantiated for at most 8 tokens per thread
+// (T <= 2048) and at most 16 (T <= kFusedMaxTokens): the tokens' slots stay in
+// registers through the whole kernel.
+constexpr int kTokPerThreadSmall = 8;
+constexpr int kTokPerThreadLarge = kFusedMaxTokens / kFThreads;
+static_assert(kTokPerThreadLarge * kFThreads == kFusedMaxTokens, "tokens per thread");
 struct IdxTables {
   int cnt[LORA_MAX_SLOTS];      // tokens per slot
   int cst[LORA_MAX_SLOTS + 1];  // first chunk of each slot; [S] = chunks
@@ -131,8 +136,12 @@ __device__ inline bool chunk_header(const int32_t* rec, int T, int S, const Chun
   return cnt > 0;
 }
 
-template <typename Elem, bool FROM_IDX>
+// TPT: 0 for the record form, else the idx form with at most TPT tokens per
+// thread.
+template <typename Elem, int TPT>
 __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
+  constexpr bool FROM_IDX = TPT > 0;
+  constexpr int kTokPerThread = TPT > 0 ? TPT : 1;
   __shared__ __attribute__((aligned(1024))) char s_lds[kWaves * kFRing];
   __shared__ int s_tok[16];
   __shared__ IdxTables s_it;
@@ -145,15 +154,17 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   bool rec_ok = false;
   int na = 0;
   int64_t n_g = 0, n_chunks = 0;
-  // idx mode: this thread's tokens t_first .. t_first + kTokPerThread - 1 and
+  // idx mode: this thread's tokens t_first .. t_first + tpt - 1 (tpt =
+  // ceil(T / threads), so that small batches spread over every thread) and
   // their slots (-1: no valid slot)
-  const int t_first = tid * kTokPerThread;
+  const int tpt = (T + kFThreads - 1) / kFThreads;
+  const int t_first = tid * tpt;
   int keys[kTokPerThread];
   if constexpr (FROM_IDX) {
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i) {
       const int t = t_first + i;
-      const int k = t < T ? f.idx[t] : -1;
+      const int k = i < tpt && t < T ? f.idx[t] : -1;
       keys[i] = k >= 0 && k < S ? k : -1;
     }
     for (int s = tid; s < S; s += kFThreads) s_it.cnt[s] = 0;
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   // build of the segment kernel -- the first workgroup with neither producer
   // nor consumer units, else the last one (which then does its units after)
   if constexpr (FROM_IDX) {
-    static_assert(sizeof(BuildShared) <= sizeof(s_lds), "the build's tables fit the rings' LDS");
+    static_assert(sizeof(BuildShared<kTokPerThread>) <= sizeof(s_lds), "the build's tables fit the rings' LDS");
     if (f.rec_out) {
       const ExpandParams& eb = f.ep;
       int64_t pairs = 0;
@@ -246,8 +257,8 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       const int64_t ge = min(G, max((int64_t)kXcds, ceil_div(pairs, kXcds) * kXcds));
       const int64_t builder = n_su + n_z < G - ge ? n_su + n_z : G - 1;
       if (blockIdx.x == builder) {
-        build_segments_block<kFThreads, kFusedMaxTokens>(f.idx, T, S, LORA_MODE_AUTO, f.rec_out,
-                                                         *reinterpret_cast<BuildShared*>(s_lds));
+        build_segments_block<kFThreads, kTokPerThread * kFThreads>(
+            f.idx, T, S, LORA_MODE_AUTO, f.rec_out, *reinterpret_cast<BuildShared<kTokPerThread>*>(s_lds));
         __syncthreads();  // the rings' LDS is used again below
       }
     }
@@ -454,12 +465,12 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   }
 }
 
-template <typename Elem, bool FROM_IDX>
+template <typename Elem, int TPT>
 hipError_t fused_launch(const FusedParams& f, hipStream_t stream) {
-  const void* kernel = reinterpret_cast<const void*>(&fused_kernel<Elem, FROM_IDX>);
+  const void* kernel = reinterpret_cast<const void*>(&fused_kernel<Elem, TPT>);
   // the grid is what the chip holds at once: consumers wait for producers
   const int grid = persistent_grid(kernel, kFThreads, 0, INT64_MAX / 4);
-  hipLaunchKernelGGL((fused_kernel<Elem, FROM_IDX>), dim3(grid), dim3(kFThreads), 0, stream, f);
+  hipLaunchKernelGGL((fused_kernel<Elem, TPT>), dim3(grid), dim3(kFThreads), 0, stream, f);
   return hipGetLastError();
 }
 
@@ -505,10 +516,17 @@ hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParam
     const long v = strtol(e, nullptr, 10);
     if (v >= 0 && v < kSpinLimit) f.spin_limit = (int)v;
   }
-  const bool from_idx = idx != nullptr;
+  // record form, or the idx form with at most 8 or 16 tokens per thread
+  const int tpt = idx == nullptr ? 0 : (sp.T <= kTokPerThreadSmall * kFThreads ? kTokPerThreadSmall : kTokPerThreadLarge);
   switch (dt) {
-    case LORA_F16: return from_idx ? fused_launch<half_t, true>(f, stream) : fused_launch<half_t, false>(f, stream);
-    case LORA_BF16: return from_idx ? fused_launch<bf16_t, true>(f, stream) : fused_launch<bf16_t, false>(f, stream);
+    case LORA_F16:
+      return tpt == 0 ? fused_launch<half_t, 0>(f, stream)
+                      : tpt == kTokPerThreadSmall ? fused_launch<half_t, kTokPerThreadSmall>(f, stream)
+                                                  : fused_launch<half_t, kTokPerThreadLarge>(f, stream);
+    case LORA_BF16:
+      return tpt == 0 ? fused_launch<bf16_t, 0>(f, stream)
+                      : tpt == kTokPerThreadSmall ? fused_launch<bf16_t, kTokPerThreadSmall>(f, stream)
+                                                  : fused_launch<bf16_t, kTokPerThreadLarge>(f, stream);
     default: return hipErrorInvalidValue;
   }
 }

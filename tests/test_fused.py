@@ -72,9 +72,9 @@ def _idx_cases():
     yield "build_kernel_S600", random_problem(rng, T=900, D=128, out_sizes=(64,), r_max=16, S=600,
                                               dtype="f16")
     # largest one-launch batch with the build inside; then two launches
-    yield "in_launch_T2048", random_problem(rng, T=2048, D=256, out_sizes=(128,), r_max=16, S=256,
+    yield "in_launch_T4096", random_problem(rng, T=4096, D=256, out_sizes=(128,), r_max=16, S=256,
                                             dtype="bf16")
-    yield "two_launches_T2100", random_problem(rng, T=2100, D=256, out_sizes=(128,), r_max=16, S=40,
+    yield "two_launches_T4200", random_problem(rng, T=4200, D=256, out_sizes=(128,), r_max=16, S=40,
                                                dtype="f16")
     yield "fp32_two_launches", random_problem(rng, T=200, D=64, out_sizes=(32,), r_max=8, S=5,
                                               dtype="f32", bad_idx_frac=0.1)
