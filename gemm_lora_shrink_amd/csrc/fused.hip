@@ -25,11 +25,12 @@
 // lines, written by one producer unit).  The other consumers of the chunk then
 // hit in L2.  (Release and acquire fences at agent scope would instead write
 // back or invalidate a whole L2 per wave, which costs far more than the
-// layer.)  Every workgroup
-// runs all of its producer units before any consumer unit, and the grid is
-// no larger than what the chip holds at once, so every producer runs while
-// consumers wait; a wait still gives up after a bounded number of polls (and
-// counts itself in the workspace's error word), so every wave exits.
+// layer.)
+//   Every workgroup runs all of its producer units before any consumer unit,
+// and the grid is no larger than what the chip holds at once, so every
+// producer runs while consumers wait; a wait still gives up after a bounded
+// number of polls (and counts itself in the workspace's error word), so every
+// wave exits.
 //   The counters start at zero.  Consumers add their column tiles to the same
 // counter, and the one that brings it to its final value (every part and
 // every column tile of the chunk) sets it back to zero, so the next call
@@ -37,6 +38,10 @@
 // depends only on its size (counters in its first quarter, after a 256-byte
 // header), so calls of any shape on one workspace use the same counter region
 // and never write their slabs over another call's counters.
+//   The chunks come from the batch's segment record (record form) or, when
+// the call is given idx (idx form), from a grouping every workgroup builds in
+// LDS; in the idx form one workgroup with no unit of its own also builds the
+// record (segments_block.h) for the batch's later layers.
 #include <stdlib.h>
 
 #include "common.h"
