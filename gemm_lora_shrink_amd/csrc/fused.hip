@@ -239,10 +239,12 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   // K parts: enough producer units to cover the grid, at most kFusedUnits
   // slabs, and at least one batch of two K steps per wave in every part
   const int n_steps = (p.D + 4 * Traits<Elem>::kVec - 1) / (4 * Traits<Elem>::kVec);
+  // (32-bit arithmetic: a 64-bit division is a long instruction sequence,
+  // and these sit on the producers' path)
   int kp = 1;
   if (n_chunks > 0) {
-    const int64_t want = min(G, (int64_t)kFusedUnits) / (n_chunks * ns);
-    kp = (int)max((int64_t)1, min(want, (int64_t)min(kMaxParts, max(1, n_steps / (2 * kWaves)))));
+    const int want = (int)min(G, (int64_t)kFusedUnits) / ((int)n_chunks * ns);
+    kp = max(1, min(want, min(kMaxParts, max(1, n_steps / (2 * kWaves)))));
   }
   const int per_part = (n_steps + kp - 1) / kp;
   const int64_t n_su = n_chunks * kp * ns;
@@ -299,9 +301,10 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       }
       continue;
     }
-    const int slice = (int)(u % ns);
-    const int part = (int)((u / ns) % kp);
-    const int64_t chunk = u / ns / kp;
+    const uint32_t uu = (uint32_t)u, un = uu / (uint32_t)ns;  // 32-bit, as above
+    const int slice = (int)(uu - un * (uint32_t)ns);
+    const int part = (int)(un % (uint32_t)kp);
+    const int64_t chunk = un / (uint32_t)kp;
     int s, cnt;
     if constexpr (FROM_IDX) {
       idx_chunk(chunk, s, cnt);
@@ -372,8 +375,9 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
     while (sl < ns && pos >= base + n_chunks * width()) next_block();
     if (sl >= ns) break;
     const int nc = n_cols(sl), cb = width();
-    const int64_t chunk = (pos - base) / cb;
-    const int ct_begin = c0 + (int)((pos - base) % cb);
+    const uint32_t rel = (uint32_t)(pos - base), rq = rel / (uint32_t)cb;  // 32-bit division
+    const int64_t chunk = rq;
+    const int ct_begin = c0 + (int)(rel - rq * (uint32_t)cb);
     const int ct_end = (int)min((int64_t)c0 + cb, ct_begin + (w1 - pos));
     pos += ct_end - ct_begin;
     int s, cnt, tok_n, ytok0, ytok1;
