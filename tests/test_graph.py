@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import gemm_lora_shrink_amd as glsa
-from gpu_util import V_TOL, Y_TOL, oracle_ref, rel_err, sample_tokens, say
+from gpu_util import V_TOL, Y_TOL, fused_counter_bytes, oracle_ref, rel_err, sample_tokens, say
 from workloads import make_workload
 from workloads.torch_io import from_torch, problem_to_device
 import oracle
@@ -102,3 +102,80 @@ def test_graph_replays_match_eager(name):
             v_ref, y_ref = refs[li]
             assert rel_err(vg[:, rows], v_ref) <= V_TOL, f"{name} replay {rep}: v vs oracle"
             assert rel_err(yg[rows], y_ref) <= Y_TOL[p.dtype], f"{name} replay {rep}: y vs oracle"
+
+
+def test_two_graphs_chosen_by_host_flag():
+    """The serving pattern of "[LoRA] LoRA cuda graph specialization"
+    (Implementation): one graph captured with the LoRA call live, one with
+    the host flag saying no adapter is active, and per step the host picks.
+    The base layer's output is stood in for by a copy into y.  Steps
+    alternate between a mixed batch (LoRA graph), an all-base batch (base
+    graph) and an all-base batch sent to the LoRA graph anyway, whose kernels
+    read the record they build and leave every row untouched."""
+    wl = make_workload("decode_qproj")
+    p = wl.problems[0]
+    say(f"[graph] two graphs decode_qproj T={p.T} S={p.S}")
+    d = problem_to_device(p, "cuda")
+    y_base = d["y"].clone()                       # the base layer's output
+    idx_mixed = d["idx"].clone()
+    idx_none = torch.full_like(idx_mixed, -1)
+    idx = torch.empty_like(idx_mixed)             # the static input of both graphs
+    seg = glsa.alloc_segments(p.T, p.S, "cuda")
+    ws = glsa.alloc_workspace(p.T, p.S, p.n_slices, p.r_max, "cuda")
+    v = torch.empty((p.n_slices, p.T, p.r_max), dtype=torch.float32, device="cuda")
+
+    def step(active):
+        d["y"].copy_(y_base)
+        glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], seg, p.out_offsets, workspace=ws,
+                           scale=d["scale"], ranks=d["ranks"], v=v, idx=idx, active=active)
+
+    idx.copy_(idx_mixed)
+    step(True)
+    torch.cuda.synchronize()
+    y_eager = oracle.decode(from_torch(d["y"], p.dtype), p.dtype)
+    rec_eager = _specified(seg, p.T, p.S)
+    rows = sample_tokens(p.idx, p.S, 64)
+    v_ref, y_ref = oracle_ref(p, tokens=rows)
+
+    graphs = {}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(True)
+        step(False)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for flag in (True, False):
+        graphs[flag] = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graphs[flag]):
+            step(flag)
+    torch.cuda.synchronize()
+
+    base_bits = from_torch(y_base, p.dtype)
+    for k, (batch, flag) in enumerate([("mixed", True), ("none", False), ("mixed", True),
+                                       ("none", True), ("none", False), ("mixed", True)]):
+        idx.copy_(idx_mixed if batch == "mixed" else idx_none)
+        d["y"].fill_(float("nan"))
+        v.fill_(float("nan"))
+        seg.fill_(-7)
+        torch.cuda.synchronize()
+        graphs[flag].replay()
+        torch.cuda.synchronize()
+        assert glsa.workspace_errors(ws) == 0, f"step {k}: a wait gave up"
+        assert not torch.any(ws[:fused_counter_bytes(ws)]).item(), f"step {k}: counters not at zero"
+        y_bits = from_torch(d["y"], p.dtype)
+        if batch == "none":
+            assert np.array_equal(y_bits, base_bits), f"step {k} ({batch}, {flag}): y changed"
+            if not flag:
+                # nothing of the library ran: v and the record keep the poison
+                assert torch.all(torch.isnan(v)).item(), f"step {k}: v written by the base graph"
+                assert torch.all(seg == -7).item(), f"step {k}: record written by the base graph"
+            else:
+                assert int(seg[0].item()) == 0, f"step {k}: record counts active tokens"
+            continue
+        assert np.array_equal(_specified(seg, p.T, p.S), rec_eager), f"step {k}: record"
+        yg = oracle.decode(y_bits, p.dtype)
+        assert rel_err(yg, y_eager) <= Y_TOL[p.dtype] / 2, f"step {k}: y differs from eager"
+        assert rel_err(yg[rows], y_ref) <= Y_TOL[p.dtype], f"step {k}: y vs oracle"
+        vg = v.cpu().numpy().astype(np.float64)
+        assert rel_err(vg[:, rows], v_ref) <= V_TOL, f"step {k}: v vs oracle"
