@@ -27,6 +27,7 @@ namespace {
 constexpr int kThreads = kUnitThreads;
 constexpr int kZeroRows = 64;  // tail entries per zero unit
 constexpr int kRingBytes = 16384;  // LDS ring of one wave (also holds its partial sums)
+constexpr int kLongK = 8192;       // contractions at least this long may be cut along K at mid sizes
 
 // Token / rank pieces and K parts of every item of a list.
 struct Split {
@@ -42,11 +43,13 @@ struct Split {
 // disjoint v rows and columns, so they need no atomics; a token piece re-reads
 // the slot's A rows and a rank piece the item's x rows, from L2.  Splitting
 // stops short of a second round: every unit pays a fixed set-up and drain.
-// cleared: v was cleared beforehand (tiny batches).  Then lists still short
-// of about three quarters of the grid are also cut into K parts (units of
-// their own, each with at least two K steps per wave) whose partial sums are
-// added with atomics; otherwise zero units clear the rows of tokens without
-// an adapter.
+// cleared: v was cleared beforehand (tiny batches, or long contractions;
+// 2 for the latter).  Then lists still short of about three quarters of the
+// grid are also cut into K parts (units of their own, each with at least two
+// K steps per wave) whose partial sums are added with atomics; otherwise zero
+// units clear the rows of tokens without an adapter.  With long contractions
+// gather groups are not cut into rank pieces: K parts fill the grid instead,
+// without every rank piece re-reading the group's x rows.
 template <typename Elem>
 __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int use_tiles, int use_groups,
                                                             int resident, int cleared) {
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int
       // candidate cuts: tiles (tokens or ranks), groups (ranks)
       const bool t_tok = tok_t > 16 && (tok_t >= rk_t || rk_t % 32 != 0);
       const bool t_ok = u_t > 0 && (t_tok || rk_t % 32 == 0) && u_t * 2 + u_g <= resident;
-      const bool g_ok = u_g > 0 && rk_g % 32 == 0 && u_t + u_g * 2 <= resident;
+      const bool g_ok = cleared != 2 && u_g > 0 && rk_g % 32 == 0 && u_t + u_g * 2 <= resident;
       if (t_ok && (!g_ok || tok_t + rk_t >= kGroup + rk_g)) {
         if (t_tok) {
           sp_t.ts *= 2;
@@ -193,15 +196,19 @@ hipError_t launch(const ShrinkParams& p, bool groups, bool tiles, hipStream_t st
   // batch of nothing but full tiles, with every piece cut, would give fewer
   // units than about three quarters of the compute units, items may also be
   // cut along K: v is cleared first.  (Mid-size batches, which would fill the
-  // compute units once, run faster without the atomics.)
+  // compute units once, run faster without the atomics -- unless the
+  // contraction is long, D >= kLongK: then a unit streams so many bytes that
+  // one round of them is slower than K parts and their atomics.)
   const int resident = persistent_grid(kernel, kThreads, 0, INT64_MAX / 4);
-  const bool cleared = ceil_div(p.T, kTile) * p.n_slices * (kTile / 16) * ceil_div(p.r_max, 16) < resident * 3 / 8;
+  const int64_t pieces = ceil_div(p.T, kTile) * p.n_slices * (kTile / 16) * ceil_div(p.r_max, 16);
+  const bool long_k = p.D >= kLongK && pieces <= resident;
+  const bool cleared = pieces < resident * 3 / 8 || long_k;
   if (cleared) {
     hipError_t e = launch_fill_zero(p.v, (int64_t)p.n_slices * p.v_slice_stride, stream);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(shrink_kernel<Elem>, dim3(resident), dim3(kThreads), 0, stream, p, tiles ? 1 : 0,
-                     groups ? 1 : 0, resident, cleared ? 1 : 0);
+                     groups ? 1 : 0, resident, long_k ? 2 : (cleared ? 1 : 0));
   return hipGetLastError();
 }
 

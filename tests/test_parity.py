@@ -86,6 +86,10 @@ def edge_problems():
         yield f"wide_D_{mode}", random_problem(
             rng, T=90, D=14336, out_sizes=(128,), r_max=64, S=2, dtype="f16",
             with_ranks=True), mode
+    # mid-size batch with a long contraction: cut along K with atomics
+    yield "long_K_mid_size", random_problem(
+        rng, T=1000, D=8192, out_sizes=(64,), r_max=64, S=20, dtype="bf16",
+        with_ranks=True), "auto"
     yield "one_token", random_problem(rng, T=1, D=8, out_sizes=(8,), r_max=8, S=1,
                                       dtype="f16", base_frac=0.0), "auto"
     yield "all_base_active_hint", random_problem(
