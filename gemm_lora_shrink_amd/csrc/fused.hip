@@ -92,6 +92,7 @@ static_assert(kTokPerThreadLarge * kFThreads == kFusedMaxTokens, "tokens per thr
 struct IdxTables {
   int cnt[LORA_MAX_SLOTS];      // tokens per slot
   int cst[LORA_MAX_SLOTS + 1];  // first chunk of each slot; [S] = chunks
+  int rank[LORA_MAX_SLOTS];     // each slot's rank, loaded beside idx
   int scan[kWaves];
   int slot;
 };
@@ -172,7 +173,12 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       const int k = i < tpt && t < T ? f.idx[t] : -1;
       keys[i] = k >= 0 && k < S ? k : -1;
     }
-    for (int s = tid; s < S; s += kFThreads) s_it.cnt[s] = 0;
+    // the slots' ranks are requested with idx, so that a unit's rank costs no
+    // memory round trip of its own once its slot is known
+    for (int s = tid; s < S; s += kFThreads) {
+      s_it.cnt[s] = 0;
+      s_it.rank[s] = slot_rank(p.ranks, s, r_max);
+    }
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i)
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       if (tid < 16) s_tok[tid] = tid < cnt ? (tw < 0 ? 0 : (tw >= T ? T - 1 : tw)) : -1;
       __syncthreads();
     }
-    const int r = __builtin_amdgcn_readfirstlane(slot_rank(p.ranks, s, r_max));
+    const int r = __builtin_amdgcn_readfirstlane(FROM_IDX ? s_it.rank[s] : slot_rank(p.ranks, s, r_max));
     if (r == 0) continue;  // consumers skip such chunks too
     const int s0 = min(n_steps, part * per_part), s1 = min(n_steps, s0 + per_part);
     float* slab = f.part + ((slice * n_chunks + chunk) * kp + part) * slab_floats;
@@ -397,7 +403,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       ytok1 = tok(yr + 8, tw_y1);
       s = __builtin_amdgcn_readfirstlane(it.slot);
     }
-    const int r = __builtin_amdgcn_readfirstlane(slot_rank(e.ranks, s, r_max));
+    const int r = __builtin_amdgcn_readfirstlane(FROM_IDX ? s_it.rank[s] : slot_rank(e.ranks, s, r_max));
     const bool write_v = f.v_out && ct_begin == 0 && wave == 0;
     float* vrow = f.v_out ? f.v_out + (int64_t)sl * p.v_slice_stride + (int64_t)(tok_n >= 0 ? tok_n : 0) * r_max
                           : nullptr;
