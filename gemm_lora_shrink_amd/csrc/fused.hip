@@ -355,8 +355,18 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
     max_cols = max(max_cols, n_cols(i));
     max_out = max(max_out, e.out_size[i]);
   }
-  const int64_t Ge = min(G, max((int64_t)kXcds, ceil_div(P, kXcds) * kXcds));
-  const int64_t ci = G - 1 - blockIdx.x;  // consumer order: the last workgroup first
+  int64_t Ge = min(G, max((int64_t)kXcds, ceil_div(P, kXcds) * kXcds));
+  int64_t ci = G - 1 - blockIdx.x;  // consumer order: the last workgroup first
+  if (TPT == kTokPerThreadLarge && f.rec_out && n_su + n_z >= G - Ge && G >= 2 * kXcds) {
+    // the record's builder is the last workgroup (the same test as above) and
+    // the batch is large (T > 2048): the last row of kXcds workgroups takes no
+    // share, so that the build, which then runs longer than a share, is not
+    // followed by one (zipf_many 60 -> 54 us; at T = 1024 the build is
+    // shorter and the row's shares are worth more)
+    Ge = min(Ge, G - kXcds);
+    ci -= kXcds;
+    if (ci < 0) return;  // uniform
+  }
   const int64_t lb = ci / kXcds;
   if (lb >= Ge / kXcds) return;  // uniform: no share
   const int64_t k = (ci % kXcds) * (Ge / kXcds) + lb;  // ci % 8 names the XCD (G is a multiple of 8)
