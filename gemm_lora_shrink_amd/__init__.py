@@ -80,6 +80,8 @@ def _load():
     lib.lora_shrink_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp, i32,
                                        i32, vp, vp, vp, vp, i32, vp, vp, i64, vp, sz, vp]
     lib.lora_shrink_expand.restype = ctypes.c_int
+    lib.lora_workspace_errors.argtypes = [vp, vp, vp]
+    lib.lora_workspace_errors.restype = ctypes.c_int
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_last_error.argtypes = []
@@ -109,6 +111,49 @@ def _check(status):
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _on_device(t, device):
+    """True when t lives in the memory of GPU `device`."""
+    return t.device.type == "cuda" and t.device == device
+
+
+def _check_tensor(t, name, device, *, dtype=None, min_numel=None, min_bytes=None):
+    """Reject, before anything reaches the library, a tensor the kernels would
+    misread: not on the call's GPU (a host address faults a kernel), another
+    dtype (int64 ranks or float64 scales would be read as 32-bit words), not
+    contiguous, or too small for what the call reads or writes.  The C ABI
+    takes bare pointers and cannot check any of this itself."""
+    if t is None:
+        return
+    if not _on_device(t, device):
+        raise LoraError(LORA_ERR_INVALID_ARG, f"{name} must be on {device} (it is on {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise LoraError(LORA_ERR_INVALID_ARG, f"{name} must be {dtype} (it is {t.dtype})")
+    if not t.is_contiguous():
+        raise LoraError(LORA_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if min_numel is not None and t.numel() < min_numel:
+        raise LoraError(LORA_ERR_INVALID_ARG, f"{name} has {t.numel()} elements, the call needs {min_numel}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise LoraError(LORA_ERR_INVALID_ARG,
+                        f"{name} has {t.numel() * t.element_size()} bytes, the call needs {min_bytes}")
+
+
+def _check_rows(t, name, device):
+    """x or y: on the call's GPU (row strides are checked by _rows)."""
+    if not _on_device(t, device):
+        raise LoraError(LORA_ERR_INVALID_ARG, f"{name} must be on {device} (it is on {t.device})")
+
+
+def _check_slot_tables(device, S, ranks, scale=None):
+    _check_tensor(ranks, "ranks", device, dtype=torch.int32, min_numel=S)
+    _check_tensor(scale, "scale", device, dtype=torch.float32, min_numel=S)
+
+
+def _check_record(seg, T, S, device):
+    if seg is None:
+        raise LoraError(LORA_ERR_INVALID_ARG, "segment record is missing")
+    _check_tensor(seg, "seg", device, min_bytes=segments_bytes(T, S))
 
 
 def _stream(stream, device):
@@ -159,6 +204,12 @@ def build_segments(idx, S, *, mode="auto", seg=None, info_host=None, stream=None
     T = idx.numel()
     if seg is None:
         seg = alloc_segments(T, S, idx.device)
+    _check_tensor(idx, "idx", idx.device)
+    _check_record(seg, T, S, idx.device)
+    if info_host is not None and (info_host.device.type != "cpu" or not info_host.is_pinned()
+                                  or info_host.dtype != torch.int32 or info_host.numel() < INFO_WORDS
+                                  or not info_host.is_contiguous()):
+        raise LoraError(LORA_ERR_INVALID_ARG, "info_host must be pinned host memory of 16 int32")
     st = _load().lora_build_segments(_ptr(idx), T, S, MODES[mode], _ptr(seg),
                                      _ptr(info_host), _stream(stream, idx.device))
     _check(st)
@@ -192,6 +243,13 @@ def shrink(x, A, seg, *, scale=None, ranks=None, v=None, active=True, stream=Non
         v = torch.empty((len(A), T, r_max), dtype=torch.float32, device=x.device)
     if v.dtype != torch.float32 or not v.is_contiguous() or v.shape != (len(A), T, r_max):
         raise LoraError(LORA_ERR_INVALID_ARG, "v must be contiguous float32 [n_slices, T, r_max]")
+    dev = x.device
+    _check_rows(x, "x", dev)
+    for i, a in enumerate(A):
+        _check_tensor(a, f"A[{i}]", dev)
+    _check_tensor(v, "v", dev)
+    _check_slot_tables(dev, S, ranks, scale)
+    _check_record(seg, T, S, dev)
     ptrs = (ctypes.c_void_p * len(A))(*[a.data_ptr() for a in A])
     st = _load().lora_shrink(_dtype_code(x), _ptr(x), ldx, T, D, len(A), ptrs, S, r_max,
                              _ptr(ranks), _ptr(scale), _ptr(seg), 1 if active else 0,
@@ -217,6 +275,16 @@ def expand(v, B, y, seg, out_offsets, *, ranks=None, active=True, v_slice_stride
     if v_slice_stride is None:
         v_slice_stride = T * r_max if v.dim() == 3 and v.size(0) > 1 else 0
     n = len(B)
+    if len(out_offsets) != n:
+        raise LoraError(LORA_ERR_INVALID_ARG, "one output offset per slice")
+    dev = y.device
+    _check_rows(y, "y", dev)
+    for i, b in enumerate(B):
+        _check_tensor(b, f"B[{i}]", dev)
+    # the kernels read rows of r_max floats of every slice's v
+    _check_tensor(v, "v", dev, min_numel=(n - 1) * max(int(v_slice_stride), 0) + T * r_max)
+    _check_slot_tables(dev, S, ranks)
+    _check_record(seg, T, S, dev)
     ptrs = (ctypes.c_void_p * n)(*[b.data_ptr() for b in B])
     sizes = (ctypes.c_int64 * n)(*[b.shape[1] for b in B])
     offs = (ctypes.c_int64 * n)(*[int(o) for o in out_offsets])
@@ -255,8 +323,19 @@ def alloc_workspace(T, S, n_slices, r_max, device):
 
 
 def workspace_errors(ws):
-    """Device-side waits that gave up in calls on this workspace (0 normally)."""
+    """Device-side waits that gave up in calls on this workspace (0 normally).
+    Synchronises with the workspace's stream."""
     return int(ws[:4].view(torch.int32).item())
+
+
+def workspace_errors_async(ws, host_out, *, stream=None):
+    """Enqueue a copy of the workspace's give-up count into host_out (pinned
+    int32 host tensor of >= 1 element); read it after the stream syncs."""
+    if host_out.device.type != "cpu" or not host_out.is_pinned() or host_out.dtype != torch.int32:
+        raise LoraError(LORA_ERR_INVALID_ARG, "host_out must be a pinned int32 host tensor")
+    _check_tensor(ws, "workspace", ws.device, dtype=torch.uint8, min_bytes=256)
+    _check(_load().lora_workspace_errors(_ptr(ws), _ptr(host_out), _stream(stream, ws.device)))
+    return host_out
 
 
 def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=None, v=None,
@@ -291,6 +370,19 @@ def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=
         raise LoraError(LORA_ERR_INVALID_ARG, "idx must be a contiguous int32 tensor of T entries")
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise LoraError(LORA_ERR_INVALID_ARG, "workspace must be a contiguous uint8 tensor")
+    if len(out_offsets) != len(B):
+        raise LoraError(LORA_ERR_INVALID_ARG, "one output offset per slice")
+    dev = x.device
+    _check_rows(x, "x", dev)
+    _check_rows(y, "y", dev)
+    for i, (a, b) in enumerate(zip(A, B)):
+        _check_tensor(a, f"A[{i}]", dev)
+        _check_tensor(b, f"B[{i}]", dev)
+    _check_tensor(v, "v", dev)
+    _check_tensor(idx, "idx", dev)
+    _check_slot_tables(dev, S, ranks, scale)
+    _check_record(seg, T, S, dev)
+    _check_tensor(workspace, "workspace", dev)
     n = len(A)
     a_ptrs = (ctypes.c_void_p * n)(*[a.data_ptr() for a in A])
     b_ptrs = (ctypes.c_void_p * n)(*[b.data_ptr() for b in B])

@@ -76,7 +76,7 @@ lora_status check_common(int dt, int32_t T, int32_t n_slices, int32_t S, int32_t
 
 }  // namespace
 
-int persistent_grid(const void* kernel, int block, size_t dyn_lds, int64_t max_useful) {
+int resident_workgroups(const void* kernel, int block, size_t dyn_lds) {
   // (device, kernel) -> workgroups resident at once, computed on first use
   struct Entry {
     int device;
@@ -101,10 +101,17 @@ int persistent_grid(const void* kernel, int block, size_t dyn_lds, int64_t max_u
     std::lock_guard<std::mutex> lock(mu);
     cache.push_back(Entry{dev, kernel, resident});
   }
-  int64_t g = resident;
+  return resident;
+}
+
+int persistent_grid(const void* kernel, int block, size_t dyn_lds, int64_t max_useful) {
+  // a multiple of 8 (the XCD count) no larger than what is resident at once,
+  // so that every workgroup of the launch can run at the same time (the
+  // one-launch shrink-expand relies on it); at least 8
+  int64_t g = resident_workgroups(kernel, block, dyn_lds) / kXcds * kXcds;
   const int64_t useful = ((max_useful > 0 ? max_useful : 1) + kXcds - 1) / kXcds * kXcds;
   if (g > useful) g = useful;
-  g = (g + kXcds - 1) / kXcds * kXcds;
+  if (g < kXcds) g = kXcds;
   return (int)g;
 }
 
@@ -355,7 +362,10 @@ LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t
   if (st != LORA_OK || T == 0) return st;
   if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
   hipError_t e = hipSuccess;
-  const bool one_launch = dt != LORA_F32 && T <= kFusedMaxTokens;
+  // one launch only where all of its workgroups are resident at once (its
+  // consumers wait for its producers); otherwise the separate launches
+  const bool one_launch = dt != LORA_F32 && T <= kFusedMaxTokens &&
+                          fused_coresident(dt, T, idx != nullptr && S <= kFusedBuildMaxSlots);
   if (one_launch && idx && S <= kFusedBuildMaxSlots) {
     // the launch builds the record itself, beside the layer
     e = launch_fused(dt, sp, ep, idx, ws, (int64_t)workspace_bytes, v, stream);
@@ -372,5 +382,15 @@ LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t
     }
   }
   if (e != hipSuccess) return hip_fail(e, "shrink-expand launch");
+  return LORA_OK;
+}
+
+LORA_EXPORT lora_status lora_workspace_errors(const void* workspace, int32_t* host_out, hipStream_t stream) {
+  clear_error();
+  if (!workspace || !host_out) return fail(LORA_ERR_INVALID_ARG, "workspace or host_out is null");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(LORA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const hipError_t e = hipMemcpyAsync(host_out, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "workspace error count copy");
   return LORA_OK;
 }

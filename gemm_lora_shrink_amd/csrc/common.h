@@ -297,9 +297,12 @@ __device__ inline int slot_rank(const int32_t* ranks, int s, int r_max) {
   return r < 0 ? 0 : (r > r_max ? r_max : r);
 }
 
-// Workgroups of a persistent launch of `kernel`: as many as the chip holds at
-// once (occupancy x compute units of the current device), a multiple of 8,
-// and no more than `max_useful` rounded up to a multiple of 8.
+// Workgroups of `kernel` the current device holds at once (occupancy x
+// compute units), computed once per device and kernel.
+int resident_workgroups(const void* kernel, int block, size_t dyn_lds);
+// Workgroups of a persistent launch of `kernel`: what the chip holds at once
+// rounded down to a multiple of 8, no more than `max_useful` rounded up to a
+// multiple of 8, and at least 8.
 int persistent_grid(const void* kernel, int block, size_t dyn_lds, int64_t max_useful);
 
 // Host-side launchers (defined in the .hip files).
@@ -333,5 +336,9 @@ int64_t fused_need_bytes(int64_t T, int64_t S, int64_t n_slices, int64_t r_max);
 // record into sp.rec (S <= kFusedBuildMaxSlots); the record is not read.
 hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, const int32_t* idx, char* ws,
                         int64_t ws_bytes, float* v_out, hipStream_t stream);
+// Whether every workgroup of the one-launch kernel for (dt, T, idx form) fits
+// on the current device at once, which its waits need; when it does not, the
+// call runs as separate launches.
+bool fused_coresident(lora_dtype dt, int32_t T, bool from_idx);
 
 }  // namespace lora

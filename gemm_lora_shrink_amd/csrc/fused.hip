@@ -491,10 +491,25 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
 }
 
 template <typename Elem, int TPT>
+const void* fused_kernel_ptr() {
+  return reinterpret_cast<const void*>(&fused_kernel<Elem, TPT>);
+}
+
+template <typename Elem, int TPT>
+bool fused_fits() {
+  // the grid (a multiple of 8, at least 8) must be resident at once, and the
+  // consumer shares assume at least two rows of 8 workgroups
+  const void* kernel = fused_kernel_ptr<Elem, TPT>();
+  const int grid = persistent_grid(kernel, kFThreads, 0, INT64_MAX / 4);
+  return grid >= 2 * kXcds && grid <= resident_workgroups(kernel, kFThreads, 0);
+}
+
+template <typename Elem, int TPT>
 hipError_t fused_launch(const FusedParams& f, hipStream_t stream) {
-  const void* kernel = reinterpret_cast<const void*>(&fused_kernel<Elem, TPT>);
+  const void* kernel = fused_kernel_ptr<Elem, TPT>();
   // the grid is what the chip holds at once: consumers wait for producers
   const int grid = persistent_grid(kernel, kFThreads, 0, INT64_MAX / 4);
+  if (!fused_fits<Elem, TPT>()) return hipErrorInvalidConfiguration;  // the caller checked fused_coresident
   hipLaunchKernelGGL((fused_kernel<Elem, TPT>), dim3(grid), dim3(kFThreads), 0, stream, f);
   return hipGetLastError();
 }
@@ -520,6 +535,21 @@ FusedLayout fused_layout(int64_t bytes) {
   W.counter_bytes = (bytes / 4) & ~int64_t(127);
   W.part = (W.counters + W.counter_bytes + 255) & ~int64_t(255);
   return W;
+}
+
+bool fused_coresident(lora_dtype dt, int32_t T, bool from_idx) {
+  const int tpt = !from_idx ? 0 : (T <= kTokPerThreadSmall * kFThreads ? kTokPerThreadSmall : kTokPerThreadLarge);
+  switch (dt) {
+    case LORA_F16:
+      return tpt == 0 ? fused_fits<half_t, 0>()
+                      : tpt == kTokPerThreadSmall ? fused_fits<half_t, kTokPerThreadSmall>()
+                                                  : fused_fits<half_t, kTokPerThreadLarge>();
+    case LORA_BF16:
+      return tpt == 0 ? fused_fits<bf16_t, 0>()
+                      : tpt == kTokPerThreadSmall ? fused_fits<bf16_t, kTokPerThreadSmall>()
+                                                  : fused_fits<bf16_t, kTokPerThreadLarge>();
+    default: return false;
+  }
 }
 
 hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, const int32_t* idx, char* ws,

@@ -10,10 +10,15 @@
 //     [D x r_s] contraction, on the matrix cores with fp32 accumulation;
 //   - zero units: 64 consecutive entries of the record's tail of tokens without
 //     an adapter, whose v rows are cleared.
-// Every v row of the batch is written exactly once with plain stores: the rows
-// of active tokens with their values (0 in rank columns k >= r_s), the others
-// with zeros.  There is no separate clearing pass and no atomic, and the result
-// does not depend on how the units are scheduled.
+// Mostly, every v row of the batch is written exactly once with plain stores:
+// the rows of active tokens with their values (0 in rank columns k >= r_s),
+// the others with zeros, with no clearing pass and no atomic, so the result
+// does not depend on how the units are scheduled.  The exception is a batch
+// whose items are cut along K (batches too small to fill the chip, and
+// mid-size batches with a contraction of at least kLongK): a clearing launch
+// then precedes the shrink, and the K parts of an item add their partial sums
+// into v with fp32 atomics in whatever order they finish, so the last bits of
+// v can differ from run to run (always within fp32 accumulation error).
 //
 // The unit itself (how its four waves split the contraction and stream the
 // operands through LDS) is in shrink_unit.h.

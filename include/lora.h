@@ -243,6 +243,17 @@ lora_status lora_expand(lora_dtype dt, const float *v, int64_t v_slice_stride, i
  * workspace and consumer units expand each chunk once every part of it is
  * there.  Larger batches and fp32 run as the shrink launch and the expand
  * launch, with v in the workspace when v is NULL.
+ * Co-residency.  The one launch's consumers wait for its producers, so it
+ * needs every one of its workgroups on the device at once: its grid is what
+ * the current device holds at once (rounded down to a multiple of 8), and
+ * where that is fewer than 16 workgroups (a partitioned or CU-masked device)
+ * the call runs as the separate launches instead.  Kernels running on other
+ * streams of the same device while the call runs take compute units the
+ * launch counts on: the call then stays correct as long as its producers
+ * still get to run within the wait bound, but it is slower, and if a wait
+ * gives up the output is invalid (counted in the workspace's word 0, readable
+ * with lora_workspace_errors).  Do not overlap a one-launch call with
+ * long-running kernels on other streams of its device.
  * Errors and the no-op gate are those of lora_shrink and lora_expand, plus
  * LORA_ERR_INVALID_ARG for a null, misaligned or short workspace.
  */
@@ -258,6 +269,19 @@ lora_status lora_shrink_expand(lora_dtype dt, const void *x, int64_t ldx, int32_
                                const void *seg, const int32_t *idx, int32_t active_hint,
                                float *v, void *y, int64_t ldy, void *workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Copy the count of waits that gave up (int32 word 0 of a lora_shrink_expand
+ * workspace) to host memory, asynchronously on `stream`, after the calls
+ * enqueued before it on that stream.
+ *   workspace  the device workspace, 256-byte aligned
+ *   host_out   [host] pinned memory of one int32; valid once the stream is
+ *              synchronised.  0 means every call on the workspace since it was
+ *              cleared produced valid output.
+ * LORA_ERR_INVALID_ARG for a null or misaligned pointer; LORA_ERR_HIP if the
+ * copy cannot be enqueued.
+ */
+lora_status lora_workspace_errors(const void *workspace, int32_t *host_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                              */

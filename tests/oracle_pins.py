@@ -110,19 +110,17 @@ def pin_expand_bruteforce(o, n_cases=150):
 # --------------------------------------------------------------------------
 
 def gather_bmv(inputs, loras, idxs):
-    """Gather each token's matrix, then one batched matrix-vector product.
+    """out[t] = loras[idxs[t]] @ inputs[t]: every token multiplied by the
+    stacked matrix its index selects, as one contraction over the gathered
+    stack.
 
-    Re-expression of the PyTorch baseline shown in "[Hardware][TPU][V1]
-    Better tpu multilora compilation" (review thread): select loras[idx],
-    drop a singleton second axis if present, multiply by the inputs viewed as
-    column vectors.  Indices must all be valid here (a -1 would pick the last
-    slot, which is why base tokens are filtered out by the caller).
+    This is the per-token gather semantics of the PyTorch baseline in
+    "[Hardware][TPU][V1] Better tpu multilora compilation" (review thread),
+    written from its definition.  loras is [S, L, D] with the input dimension
+    contiguous.  Indices must all be valid here (gathering with -1 would pick
+    the last slot, which is why the caller has no base tokens).
     """
-    sel = loras[idxs]
-    if sel.ndim == 4:
-        sel = sel[:, 0]
-    T, L, D = sel.shape
-    return np.matmul(sel, inputs.reshape(T, D, 1)).reshape(T, L)
+    return np.einsum("tld,td->tl", loras[np.asarray(idxs)], inputs)
 
 
 def pin_gather_baseline(o):
@@ -135,8 +133,7 @@ def pin_gather_baseline(o):
         xs = o.decode(p.x, "f32")
         A = o.decode(p.A[0], "f32")
         B = o.decode(p.B[0], "f32")
-        # 4-D stacked form with a singleton axis, as the baseline allows.
-        v_ref = gather_bmv(xs, A[:, None], p.idx)
+        v_ref = gather_bmv(xs, A, p.idx)
         v, y = _apply(o, p)
         _close(v[0], v_ref, 1e-13, f"gather shrink case {n}")
         d_ref = gather_bmv(v_ref, B, p.idx)

@@ -223,3 +223,114 @@ def test_fused_inactive_and_empty_are_host_side_no_ops():
     assert _fused(active=0, v=FAKE) == glsa.LORA_OK
     assert _fused(T=0) == glsa.LORA_OK
     assert _fused(active=0, D=0) == glsa.LORA_ERR_INVALID_ARG  # still validated first
+
+
+# --------------------------------------------------------------------------
+# Python binding: tensors the kernels would misread are rejected before any
+# library call (the C ABI cannot check a bare pointer's device, dtype or size)
+# --------------------------------------------------------------------------
+
+class _HostOnlyLib:
+    """The loaded library with its enqueueing entry points guarded: a call
+    reaching one fails the test, unless `allow` is set (then a call with
+    active = 0 only runs the library's host checks and enqueues nothing)."""
+    COMPUTE = {"lora_build_segments", "lora_shrink", "lora_expand", "lora_shrink_expand"}
+
+    def __init__(self, lib):
+        self._lib = lib
+        self.allow = False
+
+    def __getattr__(self, name):
+        if name in self.COMPUTE and not self.allow:
+            raise AssertionError(f"{name} was reached with an argument the binding must reject")
+        return getattr(self._lib, name)
+
+
+@pytest.fixture
+def host_only(monkeypatch):
+    import torch
+    proxy = _HostOnlyLib(glsa.lib())
+    monkeypatch.setattr(glsa, "_lib", proxy)
+    # CPU tensors stand in for device tensors of one GPU: the device test
+    # becomes "same device as x", and every other check runs as on a GPU
+    monkeypatch.setattr(glsa, "_on_device", lambda t, dev: t.device == dev)
+    T, S, D, r, out = 8, 4, 64, 16, 64
+    t = dict(
+        x=torch.zeros(T, D, dtype=torch.float16), y=torch.zeros(T, out, dtype=torch.float16),
+        A=[torch.zeros(S, r, D, dtype=torch.float16)], B=[torch.zeros(S, out, r, dtype=torch.float16)],
+        v=torch.zeros(1, T, r), ranks=torch.full((S,), r, dtype=torch.int32),
+        scale=torch.ones(S), seg=_aligned(torch, glsa.segments_bytes(T, S) // 4, torch.int32),
+        idx=torch.zeros(T, dtype=torch.int32),
+        ws=_aligned(torch, glsa.workspace_bytes(T, S, 1, r), torch.uint8))
+    return proxy, t
+
+
+def _aligned(torch, n, dtype):
+    """A zeroed host tensor of n elements at a 256-byte aligned address (the
+    library's own alignment checks still run in these tests)."""
+    esz = torch.empty(0, dtype=dtype).element_size()
+    buf = torch.zeros(n + 256 // esz, dtype=dtype)
+    skip = (-buf.data_ptr() % 256) // esz
+    return buf[skip:skip + n]
+
+
+def _call(kind, t, **over):
+    a = dict(t)
+    a.update(over)
+    if kind == "shrink":
+        return glsa.shrink(a["x"], a["A"], a["seg"], scale=a["scale"], ranks=a["ranks"], v=a["v"],
+                           active=False, stream=_NoStream())
+    if kind == "expand":
+        return glsa.expand(a["v"], a["B"], a["y"], a["seg"], [0], ranks=a["ranks"], active=False,
+                           stream=_NoStream())
+    if kind == "shrink_expand":
+        return glsa.shrink_expand(a["x"], a["A"], a["B"], a["y"], a["seg"], [0], workspace=a["ws"],
+                                  scale=a["scale"], ranks=a["ranks"], v=a["v"], idx=a["idx"],
+                                  active=False, stream=_NoStream())
+    return glsa.build_segments(a["idx"], 4, seg=a["seg"], stream=_NoStream())
+
+
+class _NoStream:
+    cuda_stream = 0
+
+
+def test_binding_accepts_valid_tensors(host_only):
+    proxy, t = host_only
+    proxy.allow = True
+    for kind in ("shrink", "expand", "shrink_expand"):
+        _call(kind, t)  # active = 0: host checks only, nothing enqueued
+
+
+@pytest.mark.parametrize("kind,field,make", [
+    ("shrink", "ranks", lambda torch, t: t["ranks"].to(torch.int64)),
+    ("shrink", "ranks", lambda torch, t: t["ranks"][:3]),
+    ("shrink", "scale", lambda torch, t: t["scale"].to(torch.float64)),
+    ("shrink", "scale", lambda torch, t: t["scale"][:2]),
+    ("shrink", "seg", lambda torch, t: t["seg"][:64]),
+    ("shrink", "A", lambda torch, t: [t["A"][0].transpose(1, 2).contiguous().transpose(1, 2)]),
+    ("expand", "v", lambda torch, t: torch.zeros(1, 4, 16)),
+    ("expand", "ranks", lambda torch, t: t["ranks"].to(torch.int16)),
+    ("expand", "seg", lambda torch, t: t["seg"][:10]),
+    ("shrink_expand", "ranks", lambda torch, t: t["ranks"].to(torch.int64)),
+    ("shrink_expand", "scale", lambda torch, t: t["scale"].double()),
+    ("shrink_expand", "seg", lambda torch, t: t["seg"][:32]),
+    ("shrink_expand", "idx", lambda torch, t: t["idx"][::2].clone()),
+    ("build_segments", "seg", lambda torch, t: t["seg"][:16]),
+], ids=lambda v: v if isinstance(v, str) else "")
+def test_binding_rejects_misread_tensors(host_only, kind, field, make):
+    import torch
+    _, t = host_only
+    with pytest.raises(glsa.LoraError):
+        _call(kind, t, **{field: make(torch, t)})
+
+
+def test_binding_rejects_host_tensors_for_device_arguments(monkeypatch):
+    """Without the stand-in, a host tensor is refused (it would be a host
+    address inside a kernel)."""
+    import torch
+    monkeypatch.setattr(glsa, "_lib", _HostOnlyLib(glsa.lib()))
+    x = torch.zeros(8, 64, dtype=torch.float16)
+    A = [torch.zeros(4, 16, 64, dtype=torch.float16)]
+    seg = glsa.alloc_segments(8, 4, "cpu")
+    with pytest.raises(glsa.LoraError, match="must be on"):
+        glsa.shrink(x, A, seg, active=False, stream=_NoStream())
