@@ -32,9 +32,10 @@
 // number of polls (and counts itself in the workspace's error word), so every
 // wave exits.
 //   The counters start at zero.  Consumers add their column tiles to the same
-// counter, and the one that brings it to its final value (every part and
+// counter, and the unit that brings it to its final value (every part and
 // every column tile of the chunk) sets it back to zero, so the next call
-// starts from zero again without a clearing pass.  The workspace layout
+// starts from zero again without a clearing pass -- also after a call in
+// which a wait gave up.  The workspace layout
 // depends only on its size (counters in its first quarter, after a 256-byte
 // header), so calls of any shape on one workspace use the same counter region
 // and never write their slabs over another call's counters.
@@ -277,6 +278,23 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
     }
   }
 
+  // A chunk's counter returns to zero once every part and every column tile
+  // of the chunk has been counted: whichever unit, producer or consumer,
+  // brings it to that final value resets it.  Consumers normally come last;
+  // a consumer whose wait gave up still counts its tiles, and then the last
+  // producer resets, so the counters are zero after every call, even one
+  // whose output was invalidated by a give-up.  A producer's returned count is
+  // checked only when the workgroup next needs thread 0 idle (its next unit,
+  // or its exit), so that the atomic's round trip is not waited for on the way
+  // to the consumer units.
+  int32_t* pend_ptr = nullptr;
+  int pend_old = 0, pend_final = 0;
+  auto settle = [&]() {
+    if (pend_ptr != nullptr && pend_old + 1 == pend_final)
+      __hip_atomic_store(pend_ptr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pend_ptr = nullptr;
+  };
+
   // ---- producer units (then zero units) on the first workgroups, which the
   // hardware dispatches first: a producer never waits, so the consumers below
   // (on the last workgroups) only ever wait for work that is running or done
@@ -333,9 +351,12 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
     // publish: every wave's slab stores are complete before the unit's count
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();  // also: the next unit rewrites s_tok and the rings
-    if (tid == 0)
-      __hip_atomic_fetch_add(f.counters + (slice * n_chunks + chunk) * kCounterStride, 1, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      settle();  // the previous unit's count has long returned
+      pend_ptr = f.counters + (slice * n_chunks + chunk) * kCounterStride;
+      pend_final = kp + (int)ceil_div(f.ep.out_size[slice], kExpandColsPerWG);
+      pend_old = __hip_atomic_fetch_add(pend_ptr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   // ---- consumer units: the pairs (slice, chunk, column tile), cut into equal
@@ -365,10 +386,16 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
     // shorter and the row's shares are worth more)
     Ge = min(Ge, G - kXcds);
     ci -= kXcds;
-    if (ci < 0) return;  // uniform
+    if (ci < 0) {  // uniform
+      if (tid == 0) settle();
+      return;
+    }
   }
   const int64_t lb = ci / kXcds;
-  if (lb >= Ge / kXcds) return;  // uniform: no share
+  if (lb >= Ge / kXcds) {  // uniform: no share
+    if (tid == 0) settle();
+    return;
+  }
   const int64_t k = (ci % kXcds) * (Ge / kXcds) + lb;  // ci % 8 names the XCD (G is a multiple of 8)
   const int64_t w0 = P * k / Ge, w1 = P * (k + 1) / Ge;
   // distinct slots in the batch (idx mode: at most the chunks and the slots)
@@ -488,6 +515,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       if (old + mine == final_count) __hip_atomic_store(cnt_ptr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  if (tid == 0) settle();
 }
 
 template <typename Elem, int TPT>

@@ -233,8 +233,9 @@ lora_status lora_expand(lora_dtype dt, const float *v, int64_t v_slice_stride, i
  *              any shape that fits, can share one workspace.  Calls that may
  *              overlap (other streams) need distinct workspaces.  int32 word 0
  *              counts device-side waits that gave up (0 in every normal run;
- *              if it is not 0 the call's output is invalid and the workspace
- *              must be cleared again).  Each wait gives up after a bounded
+ *              when a call raises it, that call's output is invalid; the
+ *              counters are still left at zero, so later calls are valid
+ *              again and leave the count unchanged).  Each wait gives up after a bounded
  *              number of polls, so a call always ends; the environment
  *              variable LORA_MI355X_FUSED_SPIN_LIMIT, when set, lowers that
  *              bound (for tests of the give-up path).
