@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
     apply(x, A, B, y, seg, out_offsets, ...) = shrink then expand
     shrink_expand(x, A, B, y, seg, out_offsets, workspace=..., ...)
                                          the same in one call (one launch for 16-bit data)
+    shrink_expand_noalloc(x, A, B, y, seg, out_offsets, ...)
+                                         the same without a workspace (allocates nothing)
     alloc_workspace(T, S, n_slices, r_max, device) -> zeroed workspace for it
 """
 
@@ -31,6 +33,9 @@ LORA_ERR_INDEX = 3
 LORA_ERR_HIP = 4
 
 MODES = {"auto": 0, "bgmv": 1, "sgmv": 2}
+# LORA_NOALLOC_SCRATCH_BYTES of include/lora.h: the per-device scratch of
+# shrink_expand_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
 SEG_FIELDS = {"info": 0, "perm": 1, "seg_slot": 2, "seg_start": 3, "groups": 4, "tiles": 5}
 INFO_WORDS = 16
 MAX_SLICES = 8
@@ -80,6 +85,9 @@ def _load():
     lib.lora_shrink_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp, i32,
                                        i32, vp, vp, vp, vp, i32, vp, vp, i64, vp, sz, vp]
     lib.lora_shrink_expand.restype = ctypes.c_int
+    lib.lora_shrink_expand_noalloc.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp,
+                                               i32, i32, vp, vp, vp, vp, i32, vp, vp, i64, vp, vp]
+    lib.lora_shrink_expand_noalloc.restype = ctypes.c_int
     lib.lora_workspace_errors.argtypes = [vp, vp, vp]
     lib.lora_workspace_errors.restype = ctypes.c_int
     lib.lora_status_string.argtypes = [ctypes.c_int]
@@ -338,16 +346,9 @@ def workspace_errors_async(ws, host_out, *, stream=None):
     return host_out
 
 
-def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=None, v=None,
-                  idx=None, active=True, stream=None):
-    """Shrink then expand in one call; y updated in place.  Returns y.
-
-    v (optional, [n_slices, T, r_max] float32) receives the intermediate.
-    idx (optional, int32 [T]): when given, the call builds the batch's segment
-    record into seg itself (as build_segments(idx, S) would) before or beside
-    the layer; without it seg must hold the record.
-    workspace: from alloc_workspace (zeroed once; every call leaves it reusable).
-    """
+def _shrink_expand_args(x, A, B, y, seg, out_offsets, scale, ranks, v, idx):
+    """Checks and marshals the arguments shared by shrink_expand and
+    shrink_expand_noalloc (everything before the workspace)."""
     A, B = list(A), list(B)
     if not A or len(A) > MAX_SLICES or len(B) != len(A):
         raise LoraError(LORA_ERR_INVALID_ARG, f"need 1..{MAX_SLICES} slices, as many B as A")
@@ -368,8 +369,6 @@ def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=
     if idx is not None and (idx.dtype != torch.int32 or idx.dim() != 1 or not idx.is_contiguous()
                             or idx.numel() != T):
         raise LoraError(LORA_ERR_INVALID_ARG, "idx must be a contiguous int32 tensor of T entries")
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-        raise LoraError(LORA_ERR_INVALID_ARG, "workspace must be a contiguous uint8 tensor")
     if len(out_offsets) != len(B):
         raise LoraError(LORA_ERR_INVALID_ARG, "one output offset per slice")
     dev = x.device
@@ -382,16 +381,47 @@ def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=
     _check_tensor(idx, "idx", dev)
     _check_slot_tables(dev, S, ranks, scale)
     _check_record(seg, T, S, dev)
-    _check_tensor(workspace, "workspace", dev)
     n = len(A)
     a_ptrs = (ctypes.c_void_p * n)(*[a.data_ptr() for a in A])
     b_ptrs = (ctypes.c_void_p * n)(*[b.data_ptr() for b in B])
     sizes = (ctypes.c_int64 * n)(*[b.shape[1] for b in B])
     offs = (ctypes.c_int64 * n)(*[int(o) for o in out_offsets])
-    st = _load().lora_shrink_expand(_dtype_code(x), _ptr(x), ldx, T, D, n, a_ptrs, b_ptrs, sizes, offs,
-                                    S, r_max, _ptr(ranks), _ptr(scale), _ptr(seg), _ptr(idx),
-                                    1 if active else 0,
-                                    _ptr(v), _ptr(y), ldy, _ptr(workspace), workspace.numel(),
-                                    _stream(stream, x.device))
+    return [_dtype_code(x), _ptr(x), ldx, T, D, n, a_ptrs, b_ptrs, sizes, offs, S, r_max,
+            _ptr(ranks), _ptr(scale), _ptr(seg), _ptr(idx)], dev, ldy
+
+
+def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=None, v=None,
+                  idx=None, active=True, stream=None):
+    """Shrink then expand in one call; y updated in place.  Returns y.
+
+    v (optional, [n_slices, T, r_max] float32) receives the intermediate.
+    idx (optional, int32 [T]): when given, the call builds the batch's segment
+    record into seg itself (as build_segments(idx, S) would) before or beside
+    the layer; without it seg must hold the record.
+    workspace: from alloc_workspace (zeroed once; every call leaves it reusable).
+    """
+    head, dev, ldy = _shrink_expand_args(x, A, B, y, seg, out_offsets, scale, ranks, v, idx)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise LoraError(LORA_ERR_INVALID_ARG, "workspace must be a contiguous uint8 tensor")
+    _check_tensor(workspace, "workspace", dev)
+    st = _load().lora_shrink_expand(*head, 1 if active else 0, _ptr(v), _ptr(y), ldy,
+                                    _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st)
+    return y
+
+
+def shrink_expand_noalloc(x, A, B, y, seg, out_offsets, *, scale=None, ranks=None, v=None,
+                          idx=None, active=True, errors_host=None, stream=None):
+    """shrink_expand without a workspace: the library's per-device scratch of
+    NOALLOC_SCRATCH_BYTES bytes stands in for it, and the call allocates
+    nothing.  Calls that may overlap on one device race.  errors_host
+    (optional pinned int32 host tensor) receives, asynchronously, the device's
+    count of waits that gave up in such calls."""
+    head, dev, ldy = _shrink_expand_args(x, A, B, y, seg, out_offsets, scale, ranks, v, idx)
+    if errors_host is not None and (errors_host.device.type != "cpu" or not errors_host.is_pinned()
+                                    or errors_host.dtype != torch.int32):
+        raise LoraError(LORA_ERR_INVALID_ARG, "errors_host must be a pinned int32 host tensor")
+    st = _load().lora_shrink_expand_noalloc(*head, 1 if active else 0, _ptr(v), _ptr(y), ldy,
+                                            _ptr(errors_host), _stream(stream, dev))
     _check(st)
     return y

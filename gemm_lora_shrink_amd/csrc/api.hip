@@ -332,13 +332,83 @@ LORA_EXPORT size_t lora_shrink_expand_workspace_bytes(int32_t T, int32_t S, int3
   return (size_t)fused_need_bytes(T, S, n_slices, r_max);
 }
 
+namespace lora {
+namespace {
+
+// The body of lora_shrink_expand and of its allocation-free variant: checks,
+// the no-op gate, then the launches on the workspace ws of ws_bytes bytes.
+// clear_first: enqueue a clearing of the workspace's header and counters
+// before the launches (the variant's first call on a device).
+lora_status shrink_expand_impl(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D, int32_t n_slices,
+                               const void* const* A, const void* const* B, const int64_t* out_sizes,
+                               const int64_t* out_offsets, int32_t S, int32_t r_max, const int32_t* ranks,
+                               const float* scale, const void* seg, const int32_t* idx, int32_t active_hint, float* v,
+                               void* y, int64_t ldy, char* ws, int64_t ws_bytes, bool clear_first,
+                               bool* ran, hipStream_t stream) {
+  *ran = false;
+  // without a caller v, the two-launch form keeps v in the workspace's data
+  // region (never in the header or the counters)
+  const FusedLayout W = fused_layout(ws_bytes);
+  float* v_eff = v ? v : reinterpret_cast<float*>(ws + W.part);
+  ShrinkParams sp;
+  lora_status st = prep_shrink(dt, x, ldx, T, D, n_slices, A, S, r_max, ranks, scale, seg, v_eff, sp);
+  if (st != LORA_OK) return st;
+  ExpandParams ep;
+  st = prep_expand(dt, v_eff, (int64_t)T * r_max, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks, seg, y,
+                   ldy, ep);
+  if (st != LORA_OK || T == 0) return st;
+  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
+  hipError_t e = hipSuccess;
+  if (clear_first) e = launch_fill_zero(reinterpret_cast<float*>(ws), W.part / 4, stream);
+  *ran = e == hipSuccess;
+  // one launch only where all of its workgroups are resident at once (its
+  // consumers wait for its producers); otherwise the separate launches
+  const bool one_launch = dt != LORA_F32 && T <= kFusedMaxTokens &&
+                          fused_coresident(dt, T, idx != nullptr && S <= kFusedBuildMaxSlots);
+  if (e != hipSuccess) {
+  } else if (one_launch && idx && S <= kFusedBuildMaxSlots) {
+    // the launch builds the record itself, beside the layer
+    e = launch_fused(dt, sp, ep, idx, ws, ws_bytes, v, stream);
+  } else {
+    // with idx and no room for the build inside the launch: the build kernel first
+    if (idx) e = launch_build_segments(idx, T, S, LORA_MODE_AUTO, static_cast<int32_t*>(const_cast<void*>(seg)), stream);
+    if (e == hipSuccess && one_launch) {
+      e = launch_fused(dt, sp, ep, nullptr, ws, ws_bytes, v, stream);
+    } else if (e == hipSuccess) {
+      // larger batches stream enough bytes per launch that the launch and the
+      // round trips no longer dominate: the shrink launch then the expand launch
+      e = launch_shrink(dt, sp, /*groups=*/true, /*tiles=*/true, stream);
+      if (e == hipSuccess) e = run_expand(dt, ep, stream);
+    }
+  }
+  if (e != hipSuccess) return hip_fail(e, "shrink-expand launch");
+  return LORA_OK;
+}
+
+// Scratch of the allocation-free variant: a file-scope device array, one copy
+// per device the library runs on, held until the process ends.  Host code
+// never uses the array's name as an address: the device address of each
+// device's copy comes from hipGetSymbolAddress, once per device, with that
+// device current.
+static __device__ __align__(256) char scratch[LORA_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchOfDevice {
+  int device;
+  char* ptr;     // device address of this device's copy of `scratch`
+  bool cleared;  // its header and counters have been cleared in stream order
+};
+std::mutex g_scratch_mu;
+std::vector<ScratchOfDevice> g_scratch;
+
+}  // namespace
+}  // namespace lora
+
 LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D,
                                            int32_t n_slices, const void* const* A, const void* const* B,
                                            const int64_t* out_sizes, const int64_t* out_offsets, int32_t S,
                                            int32_t r_max, const int32_t* ranks, const float* scale, const void* seg,
                                            const int32_t* idx, int32_t active_hint, float* v, void* y, int64_t ldy,
-                                           void* workspace,
-                                           size_t workspace_bytes, hipStream_t stream) {
+                                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
   if (st != LORA_OK) return st;
@@ -349,39 +419,67 @@ LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t
   if ((int64_t)workspace_bytes < need)
     return fail(LORA_ERR_INVALID_ARG, "workspace has %zu bytes, the call needs %lld", workspace_bytes,
                 (long long)need);
-  char* ws = static_cast<char*>(workspace);
-  // without a caller v, the two-launch form keeps v in the workspace's data
-  // region (never in the header or the counters)
-  float* v_eff = v ? v : reinterpret_cast<float*>(ws + fused_layout((int64_t)workspace_bytes).part);
-  ShrinkParams sp;
-  st = prep_shrink(dt, x, ldx, T, D, n_slices, A, S, r_max, ranks, scale, seg, v_eff, sp);
+  bool ran;
+  return shrink_expand_impl(dt, x, ldx, T, D, n_slices, A, B, out_sizes, out_offsets, S, r_max, ranks, scale, seg,
+                            idx, active_hint, v, y, ldy, static_cast<char*>(workspace), (int64_t)workspace_bytes,
+                            /*clear_first=*/false, &ran, stream);
+}
+
+LORA_EXPORT lora_status lora_shrink_expand_noalloc(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D,
+                                                   int32_t n_slices, const void* const* A, const void* const* B,
+                                                   const int64_t* out_sizes, const int64_t* out_offsets, int32_t S,
+                                                   int32_t r_max, const int32_t* ranks, const float* scale,
+                                                   const void* seg, const int32_t* idx, int32_t active_hint, float* v,
+                                                   void* y, int64_t ldy, int32_t* errors_host, hipStream_t stream) {
+  clear_error();
+  lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
   if (st != LORA_OK) return st;
-  ExpandParams ep;
-  st = prep_expand(dt, v_eff, (int64_t)T * r_max, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks, seg, y,
-                   ldy, ep);
-  if (st != LORA_OK || T == 0) return st;
-  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
-  hipError_t e = hipSuccess;
-  // one launch only where all of its workgroups are resident at once (its
-  // consumers wait for its producers); otherwise the separate launches
-  const bool one_launch = dt != LORA_F32 && T <= kFusedMaxTokens &&
-                          fused_coresident(dt, T, idx != nullptr && S <= kFusedBuildMaxSlots);
-  if (one_launch && idx && S <= kFusedBuildMaxSlots) {
-    // the launch builds the record itself, beside the layer
-    e = launch_fused(dt, sp, ep, idx, ws, (int64_t)workspace_bytes, v, stream);
-  } else {
-    // with idx and no room for the build inside the launch: the build kernel first
-    if (idx) e = launch_build_segments(idx, T, S, LORA_MODE_AUTO, static_cast<int32_t*>(const_cast<void*>(seg)), stream);
-    if (e == hipSuccess && one_launch) {
-      e = launch_fused(dt, sp, ep, nullptr, ws, (int64_t)workspace_bytes, v, stream);
-    } else if (e == hipSuccess) {
-      // larger batches stream enough bytes per launch that the launch and the
-      // round trips no longer dominate: the shrink launch then the expand launch
-      e = launch_shrink(dt, sp, /*groups=*/true, /*tiles=*/true, stream);
-      if (e == hipSuccess) e = run_expand(dt, ep, stream);
+  const int64_t need = fused_need_bytes(T, S, n_slices, r_max);
+  if (need > (int64_t)LORA_NOALLOC_SCRATCH_BYTES)
+    return fail(LORA_ERR_UNSUPPORTED,
+                "the call needs %lld bytes of scratch, more than the %lld of the allocation-free variant "
+                "(use lora_shrink_expand with a workspace)",
+                (long long)need, (long long)LORA_NOALLOC_SCRATCH_BYTES);
+  // the device address of this device's scratch (no allocation: the array is
+  // part of the loaded code object)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  char* ptr = nullptr;
+  bool cleared = false;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    for (const ScratchOfDevice& sd : g_scratch)
+      if (sd.device == dev) {
+        ptr = sd.ptr;
+        cleared = sd.cleared;
+      }
+    if (!ptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      ptr = static_cast<char*>(p);
+      g_scratch.push_back(ScratchOfDevice{dev, ptr, false});
     }
   }
-  if (e != hipSuccess) return hip_fail(e, "shrink-expand launch");
+  // The first call on a device clears the scratch's header and counters, in
+  // stream order before its launches.  A call made while the stream is being
+  // captured records that clearing in the graph (replayed with it) and does
+  // not count as the first call.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  bool ran = false;
+  st = shrink_expand_impl(dt, x, ldx, T, D, n_slices, A, B, out_sizes, out_offsets, S, r_max, ranks, scale, seg, idx,
+                          active_hint, v, y, ldy, ptr, (int64_t)LORA_NOALLOC_SCRATCH_BYTES, !cleared, &ran, stream);
+  if (ran && !cleared && cap == hipStreamCaptureStatusNone) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    for (ScratchOfDevice& sd : g_scratch)
+      if (sd.device == dev) sd.cleared = true;
+  }
+  if (st != LORA_OK || !errors_host) return st;
+  e = hipMemcpyAsync(errors_host, ptr, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "scratch error count copy");
   return LORA_OK;
 }
 

@@ -272,6 +272,42 @@ lora_status lora_shrink_expand(lora_dtype dt, const void *x, int64_t ldx, int32_
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * lora_shrink_expand without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and result as lora_shrink_expand,
+ * minus workspace and workspace_bytes; the call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).
+ *   errors_host  [host] nullable; pinned memory of one int32.  When given, the
+ *                count of device-side waits that gave up in every call of this
+ *                variant on the current device since the process started is
+ *                copied there asynchronously after the call's kernels (0 in
+ *                every normal run; see the co-residency note above).
+ * Scratch.  In place of the workspace the kernels use a device array of
+ * LORA_NOALLOC_SCRATCH_BYTES bytes that is part of the library's code object:
+ * each device the library runs on holds its own copy until the process ends.
+ * Its header and counters are cleared, in stream order, by the first call on
+ * each device made outside stream capture (a call under capture records that
+ * clearing in the graph); every call leaves its counters at zero again, so
+ * later calls need no clearing.  Every call on one device shares that
+ * device's scratch: calls that may overlap on one device (other streams, or
+ * graphs replayed concurrently) race and must be serialised by the caller.
+ * A call whose workspace would exceed LORA_NOALLOC_SCRATCH_BYTES
+ * (lora_shrink_expand_workspace_bytes(T, S, n_slices, r_max) > the limit, e.g.
+ * prefill batches of many tokens and slices) returns LORA_ERR_UNSUPPORTED
+ * and enqueues nothing.  LORA_ERR_HIP if the scratch's device address cannot
+ * be obtained.  Other errors and the no-op gate are those of
+ * lora_shrink_expand.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+lora_status lora_shrink_expand_noalloc(lora_dtype dt, const void *x, int64_t ldx, int32_t T, int32_t D,
+                                       int32_t n_slices, const void *const *A, const void *const *B,
+                                       const int64_t *out_sizes, const int64_t *out_offsets, int32_t S,
+                                       int32_t r_max, const int32_t *ranks, const float *scale,
+                                       const void *seg, const int32_t *idx, int32_t active_hint, float *v,
+                                       void *y, int64_t ldy, int32_t *errors_host, hipStream_t stream);
+
+/*
  * Copy the count of waits that gave up (int32 word 0 of a lora_shrink_expand
  * workspace) to host memory, asynchronously on `stream`, after the calls
  * enqueued before it on that stream.

@@ -334,3 +334,43 @@ def test_binding_rejects_host_tensors_for_device_arguments(monkeypatch):
     seg = glsa.alloc_segments(8, 4, "cpu")
     with pytest.raises(glsa.LoraError, match="must be on"):
         glsa.shrink(x, A, seg, active=False, stream=_NoStream())
+
+
+# --------------------------------------------------------------------------
+# lora_shrink_expand_noalloc: host-side refusals (no GPU call)
+# --------------------------------------------------------------------------
+
+def _noalloc(**kw):
+    a = dict(dt=2, x=FAKE, ldx=64, T=8, D=64, n_slices=1, A=[FAKE], B=[FAKE], sizes=[64],
+             offs=[0], S=4, r_max=16, ranks=None, scale=None, seg=FAKE, idx=None, active=1, v=None,
+             y=FAKE, ldy=64, err=None)
+    a.update(kw)
+    n = a["n_slices"]
+    A = (ctypes.c_void_p * len(a["A"]))(*a["A"])
+    B = (ctypes.c_void_p * len(a["B"]))(*a["B"])
+    sizes = (ctypes.c_int64 * len(a["sizes"]))(*a["sizes"])
+    offs = (ctypes.c_int64 * len(a["offs"]))(*a["offs"])
+    return glsa.lib().lora_shrink_expand_noalloc(
+        a["dt"], a["x"], a["ldx"], a["T"], a["D"], n, A, B, sizes, offs, a["S"], a["r_max"], a["ranks"],
+        a["scale"], a["seg"], a["idx"], a["active"], a["v"], a["y"], a["ldy"], a["err"], None)
+
+
+def test_noalloc_scratch_limit_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define LORA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == glsa.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,status", [
+    # needs more scratch than the variant has: refused before anything else
+    (dict(T=16384, n_slices=8, r_max=64, A=[FAKE] * 8, B=[FAKE] * 8, sizes=[64] * 8,
+          offs=[64 * i for i in range(8)], ldy=512), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(dt=9), glsa.LORA_ERR_INVALID_ARG),
+    (dict(seg=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(S=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(r_max=72), glsa.LORA_ERR_UNSUPPORTED),
+])
+def test_noalloc_rejects_on_the_host(kw, status):
+    assert glsa.workspace_bytes(16384, 4, 8, 64) > glsa.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(**kw) == status
+    assert glsa.lib().lora_last_error()
