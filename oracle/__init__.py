@@ -19,6 +19,8 @@ from .lora_oracle import (
     oracle_shrink,
     oracle_expand,
     oracle_apply,
+    oracle_embedding_shrink,
+    oracle_embedding_apply,
 )
 
 __all__ = [
@@ -29,4 +31,6 @@ __all__ = [
     "oracle_shrink",
     "oracle_expand",
     "oracle_apply",
+    "oracle_embedding_shrink",
+    "oracle_embedding_apply",
 ]

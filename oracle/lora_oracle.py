@@ -206,3 +206,53 @@ def oracle_apply(x, A, B, y_in, idx, S, out_offsets, *, dtype, D=None,
     y = oracle_expand(v, B, y_in, idx, S, out_offsets, dtype=dtype,
                       ranks=ranks, tokens=tokens)
     return v, y
+
+
+def oracle_embedding_shrink(tok, A_emb, idx, S, *, dtype, scale=None, ranks=None,
+                            tokens=None):
+    """Shrink of a LoRA on an embedding table, in fp64.
+
+    "Add multi-LoRA support", Features: adapters cover every linear layer and
+    the embeddings, in PEFT format.  In that format an embedding adapter of
+    slot s holds A_s (r x V) and B_s (H x r), and the input of the layer for
+    token id w is the one-hot vector e_w of length V, so the linear shrink
+    A_s @ x reduces to column w of A_s.  This library stacks the tables
+    transposed, A_emb[s] = A_s^T of shape [V][r_max] (one contiguous rank
+    vector per vocabulary row; reading), so that
+
+        v[t][k] = scale[s] * A_emb[s][tok[t]][k]          (k < r_s)
+
+    tok    [T] int token ids; an id outside [0, V) has no adapter row, and its
+           intermediate is zero (reading: such ids, e.g. tokens added by an
+           adapter, are looked up elsewhere)
+    A_emb  [S, V, r_max] storage dtype      idx [T] slots (-1: base only)
+    Returns v of shape [len(tokens), r_max], float64 (zero rows for inactive
+    tokens and for ids outside the table).
+    """
+    idx = np.asarray(idx).reshape(-1)
+    tok = np.asarray(tok).reshape(-1)
+    T = idx.shape[0]
+    V, r_max = A_emb.shape[1], A_emb.shape[2]
+    tokens = list(range(T)) if tokens is None else [int(t) for t in tokens]
+    v = np.zeros((len(tokens), r_max), dtype=np.float64)
+    for j, t in enumerate(tokens):
+        s = int(idx[t])
+        w = int(tok[t])
+        if not _valid_slot(s, S) or not 0 <= w < V:
+            continue
+        r = _rank(ranks, s, r_max)
+        sc = 1.0 if scale is None else float(np.float64(scale[s]))
+        v[j, :r] = sc * decode(A_emb[s, w, :r], dtype)
+    return v
+
+
+def oracle_embedding_apply(tok, A_emb, B, y_in, idx, S, *, dtype, scale=None,
+                           ranks=None, tokens=None):
+    """Embedding LoRA: y[t] = y_in[t] + B_s @ v[t] with v from
+    oracle_embedding_shrink (the expand is the linear layers' expand with one
+    slice of width H).  Returns (v, y) for the listed tokens."""
+    v = oracle_embedding_shrink(tok, A_emb, idx, S, dtype=dtype, scale=scale,
+                                ranks=ranks, tokens=tokens)
+    y = oracle_expand(v[None], [B], y_in, idx, S, (0,), dtype=dtype, ranks=ranks,
+                      tokens=tokens)
+    return v, y

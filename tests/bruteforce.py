@@ -96,3 +96,35 @@ def brute_expand(p, v):
                     acc += to_float(B[j, k], dt) * vt[k]
                 y[t][off + j] += acc
     return y
+
+
+def brute_embedding(p):
+    """Embedding LoRA in pure Python, through the layer's one-hot input.
+
+    For token id w the layer's input is e_w (length V); the shrink is the PEFT
+    table A_s (r x V, i.e. A_emb[s] transposed) times e_w, summed over all V
+    entries of the one-hot vector, then the expand B_s (H x r).  Returns
+    (v rows, y rows) as lists of Python floats.
+    """
+    dt = p.dtype
+    y = [to_lists(p.y_in[t], dt) for t in range(p.T)]
+    v = [[0.0] * p.r_max for _ in range(p.T)]
+    for t in range(p.T):
+        s = int(p.idx[t])
+        if not (0 <= s < p.S):
+            continue
+        w = int(p.tok[t])
+        r = p.r_max if p.ranks is None else int(p.ranks[s])
+        sc = float(p.scale[s])
+        onehot = [1.0 if c == w else 0.0 for c in range(p.V)]
+        for k in range(r):
+            acc = 0.0
+            for c in range(p.V):
+                acc += to_float(p.A_emb[s, c, k], dt) * onehot[c]
+            v[t][k] = sc * acc
+        for j in range(p.H):
+            acc = 0.0
+            for k in range(r):
+                acc += to_float(p.B[s, j, k], dt) * v[t][k]
+            y[t][j] += acc
+    return v, y

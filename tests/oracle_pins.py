@@ -16,8 +16,8 @@ import os
 
 import numpy as np
 
-from bruteforce import brute_apply, brute_expand, brute_segments
-from workloads import random_problem
+from bruteforce import brute_apply, brute_embedding, brute_expand, brute_segments
+from workloads import random_embedding_problem, random_problem
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -389,6 +389,89 @@ def pin_segments(o):
             assert np.all(idx[seg] == a["seg_slot"][g]) and np.all(np.diff(seg) > 0)
 
 
+# --------------------------------------------------------------------------
+# embedding LoRA
+# --------------------------------------------------------------------------
+
+def embedding_cases(n_cases=120, seed=55):
+    rng = np.random.default_rng(seed)
+    fixed = [dict(T=0, V=3, H=2, r_max=2, S=1), dict(T=1, V=1, H=1, r_max=1, S=1, base_frac=0.0),
+             dict(T=6, V=5, H=3, r_max=2, S=2, base_frac=1.0),
+             dict(T=9, V=7, H=4, r_max=3, S=3, bad_tok_frac=0.4, bad_idx_frac=0.2)]
+    for c in fixed:
+        yield random_embedding_problem(rng, **c)
+    dtypes = ["f32", "f16", "bf16"]
+    for n in range(n_cases - len(fixed)):
+        yield random_embedding_problem(
+            rng, T=int(rng.integers(0, 12)), V=int(rng.integers(1, 20)), H=int(rng.integers(1, 12)),
+            r_max=int(rng.integers(1, 9)), S=int(rng.integers(1, 5)), dtype=dtypes[n % 3],
+            base_frac=float(rng.uniform(0, 0.5)), with_ranks=bool(n % 2),
+            bad_tok_frac=0.15 if n % 4 == 0 else 0.0, bad_idx_frac=0.1 if n % 5 == 0 else 0.0)
+
+
+def _embedding_apply(o, p):
+    return o.oracle_embedding_apply(p.tok, p.A_emb, p.B, p.y_in, p.idx, p.S, dtype=p.dtype,
+                                    scale=p.scale, ranks=p.ranks)
+
+
+def pin_embedding_bruteforce(o):
+    """Against the one-hot product in pure Python (with garbage past each rank)."""
+    rng = np.random.default_rng(56)
+    for n, p in enumerate(embedding_cases()):
+        if p.ranks is not None:
+            for s, r in enumerate(p.ranks):
+                p.A_emb[s, :, r:] = p.A_emb.dtype.type(5) if p.A_emb.dtype != np.uint16 else np.uint16(0x40a0)
+                p.B[s, :, r:] = p.B.dtype.type(5) if p.B.dtype != np.uint16 else np.uint16(0x40a0)
+        v, y = _embedding_apply(o, p)
+        vb, yb = brute_embedding(p)
+        _close(v, np.asarray(vb, dtype=np.float64).reshape(p.T, p.r_max), 1e-12, f"embedding v case {n}")
+        _close(y, np.asarray(yb, dtype=np.float64).reshape(p.T, p.ldy), 1e-12, f"embedding y case {n}")
+
+
+def pin_embedding_is_linear_on_one_hot(o):
+    """The embedding adapter is the linear adapter applied to the one-hot rows
+    of the token ids, with the table transposed (A_s = A_emb[s]^T): checked
+    against the (separately pinned) linear oracle; ids outside [0, V) have an
+    all-zero one-hot row."""
+    rng = np.random.default_rng(57)
+    for n in range(40):
+        p = random_embedding_problem(rng, T=int(rng.integers(1, 25)), V=int(rng.integers(1, 40)),
+                                     H=int(rng.integers(1, 20)), r_max=int(rng.integers(1, 9)),
+                                     S=int(rng.integers(1, 5)), dtype=("f32", "f16", "bf16")[n % 3],
+                                     with_ranks=bool(n % 2), bad_tok_frac=0.2 if n % 3 == 0 else 0.0)
+        x = np.zeros((p.T, p.V), dtype=np.float32)
+        for t, w in enumerate(p.tok):
+            if 0 <= w < p.V:
+                x[t, w] = 1.0
+        x = x.astype(p.A_emb.dtype) if p.dtype != "bf16" else (x.view(np.uint32) >> 16).astype(np.uint16)
+        A_lin = np.ascontiguousarray(np.transpose(p.A_emb, (0, 2, 1)))
+        v_lin, y_lin = o.oracle_apply(x, [A_lin], [p.B], p.y_in, p.idx, p.S, (0,), dtype=p.dtype,
+                                      scale=p.scale, ranks=p.ranks)
+        v, y = _embedding_apply(o, p)
+        _close(v, v_lin[0], 1e-13, f"embedding vs linear v case {n}")
+        _close(y, y_lin, 1e-13, f"embedding vs linear y case {n}")
+
+
+def pin_embedding_invariants(o):
+    """Base rows and rows of ids outside the table are bit-identical to y_in;
+    the delta is linear in scale and independent of y_in."""
+    rng = np.random.default_rng(58)
+    for n in range(30):
+        p = random_embedding_problem(rng, T=30, V=11, H=6, r_max=4, S=3, dtype="f32",
+                                     bad_tok_frac=0.2, bad_idx_frac=0.1)
+        v, y = _embedding_apply(o, p)
+        y_in = o.decode(p.y_in, "f32")
+        dead = ~((p.idx >= 0) & (p.idx < p.S)) | (p.tok < 0) | (p.tok >= p.V)
+        assert np.array_equal(y[dead], y_in[dead]), f"embedding dead rows case {n}"
+        assert not np.any(v[dead]), f"embedding dead v case {n}"
+        p2 = random_embedding_problem(rng, T=30, V=11, H=6, r_max=4, S=3, dtype="f32",
+                                      idx=p.idx, tok=p.tok)
+        p2.A_emb, p2.B, p2.scale = p.A_emb, p.B, p.scale * 2
+        v2, y2 = _embedding_apply(o, p2)
+        _close(v2, 2 * v, 1e-13, f"embedding scale linearity case {n}")
+        _close(y2 - o.decode(p2.y_in, "f32"), 2 * (y - y_in), 1e-12, f"embedding delta case {n}")
+
+
 ALL_PINS = [
     pin_bruteforce,
     pin_expand_bruteforce,
@@ -403,4 +486,7 @@ ALL_PINS = [
     pin_token_subset,
     pin_handworked,
     pin_segments,
+    pin_embedding_bruteforce,
+    pin_embedding_is_linear_on_one_hot,
+    pin_embedding_invariants,
 ]

@@ -42,6 +42,14 @@ MUTANTS = {
                            "cache[key] = decode(A[i][(s + 1) % S], dtype)"),
     "half_intermediate": ("v[i, j, :r] = sc * (a[:r, :] @ xt)",
                           "v[i, j, :r] = (sc * (a[:r, :] @ xt)).astype(np.float16)"),
+    "embedding_wrong_row": ("v[j, :r] = sc * decode(A_emb[s, w, :r], dtype)",
+                            "v[j, :r] = sc * decode(A_emb[s, (w + 1) % V, :r], dtype)"),
+    "embedding_no_scale": ("v[j, :r] = sc * decode(A_emb[s, w, :r], dtype)",
+                           "v[j, :r] = decode(A_emb[s, w, :r], dtype)"),
+    "embedding_bad_id_wraps": ("if not _valid_slot(s, S) or not 0 <= w < V:",
+                               "if not _valid_slot(s, S) or not -V <= w < V:"),
+    "embedding_ignores_rank": ("v[j, :r] = sc * decode(A_emb[s, w, :r], dtype)",
+                               "v[j, :] = sc * decode(A_emb[s, w, :], dtype)"),
 }
 
 

@@ -13,6 +13,8 @@ from .gen import (
     Workload,
     make_workload,
     random_problem,
+    EmbeddingProblem,
+    random_embedding_problem,
     round_to_dtype,
     bf16_bits_to_f32,
     STORAGE_NP,
@@ -26,6 +28,8 @@ __all__ = [
     "Workload",
     "make_workload",
     "random_problem",
+    "EmbeddingProblem",
+    "random_embedding_problem",
     "round_to_dtype",
     "bf16_bits_to_f32",
     "STORAGE_NP",

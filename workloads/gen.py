@@ -207,3 +207,72 @@ def random_problem(rng, *, T, D, out_sizes, r_max, S, dtype="f32",
         A=[round_to_dtype(a, dtype) for a in A],
         B=[round_to_dtype(b, dtype) for b in B],
         y_in=round_to_dtype(y, dtype))
+
+
+@dataclass
+class EmbeddingProblem:
+    """A LoRA on an embedding table applied to one batch.
+
+    tok    [T] int32 token ids (row of the table; ids outside [0, V) allowed)
+    A_emb  [S, V, r_max]   the adapters' A tables stacked transposed (one rank
+                           vector per vocabulary row)
+    B      [S, H, r_max]   expand weights
+    y_in   [T, ldy]        embedding output rows; the delta goes to columns [0, H)
+    """
+
+    name: str
+    dtype: str
+    T: int
+    V: int
+    H: int
+    S: int
+    r_max: int
+    ldy: int
+    idx: np.ndarray
+    tok: np.ndarray
+    scale: np.ndarray
+    ranks: Optional[np.ndarray]
+    A_emb: np.ndarray
+    B: np.ndarray
+    y_in: np.ndarray
+
+    @property
+    def elem_bytes(self):
+        return ELEM_BYTES[self.dtype]
+
+
+def random_embedding_problem(rng, *, T, V, H, r_max, S, dtype="f32", base_frac=0.25,
+                             with_ranks=False, random_scale=True, bad_idx_frac=0.0,
+                             bad_tok_frac=0.0, ldy=None, w_var=1.0, y_var=1.0, tok=None,
+                             idx=None):
+    """A random embedding-LoRA batch drawn from `rng` (same conventions as
+    random_problem; a fraction bad_tok_frac of tokens gets an id outside
+    [0, V))."""
+    ldy = H if ldy is None else ldy
+    if idx is None:
+        idx = rng.integers(0, S, size=T).astype(np.int32)
+        if T:
+            idx[rng.random(T) < base_frac] = -1
+            if bad_idx_frac > 0:
+                bad = rng.random(T) < bad_idx_frac
+                idx[bad] = rng.choice(np.array([-5, S, S + 9], dtype=np.int32), size=int(bad.sum()))
+    idx = np.asarray(idx, dtype=np.int32)
+    if tok is None:
+        tok = rng.integers(0, V, size=T).astype(np.int32)
+        if T and bad_tok_frac > 0:
+            bad = rng.random(T) < bad_tok_frac
+            tok[bad] = rng.choice(np.array([-1, -7, V, V + 3], dtype=np.int32), size=int(bad.sum()))
+    tok = np.asarray(tok, dtype=np.int32)
+    ranks = rng.integers(1, r_max + 1, size=S).astype(np.int32) if with_ranks else None
+    scale = (rng.uniform(0.5, 4.0, size=S) if random_scale else np.ones(S)).astype(np.float32)
+    A = _normal(rng, w_var, (S, V, r_max))
+    B = _normal(rng, w_var, (S, H, r_max))
+    if ranks is not None:
+        for s, r in enumerate(ranks):
+            A[s, :, r:] = 0.0
+            B[s, :, r:] = 0.0
+    y = _normal(rng, y_var, (T, ldy))
+    return EmbeddingProblem(
+        name="random_embedding", dtype=dtype, T=T, V=V, H=H, S=S, r_max=r_max, ldy=ldy,
+        idx=idx, tok=tok, scale=scale, ranks=ranks, A_emb=round_to_dtype(A, dtype),
+        B=round_to_dtype(B, dtype), y_in=round_to_dtype(y, dtype))
