@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
                                          the same in one call (one launch for 16-bit data)
     shrink_expand_noalloc(x, A, B, y, seg, out_offsets, ...)
                                          the same without a workspace (allocates nothing)
+    embedding_shrink(tok, A_emb, idx, ...) -> v of an embedding adapter ([1, T, r_max])
+    embedding_apply(tok, A_emb, B_emb, y, seg, idx, ...) = embedding_shrink then expand
     alloc_workspace(T, S, n_slices, r_max, device) -> zeroed workspace for it
 """
 
@@ -88,6 +90,10 @@ def _load():
     lib.lora_shrink_expand_noalloc.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp,
                                                i32, i32, vp, vp, vp, vp, i32, vp, vp, i64, vp, vp]
     lib.lora_shrink_expand_noalloc.restype = ctypes.c_int
+    lib.lora_embedding_shrink.argtypes = [ctypes.c_int, vp, i32, i64, vp, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.lora_embedding_shrink.restype = ctypes.c_int
+    lib.lora_copy_padded.argtypes = [ctypes.c_int, vp, i64, i64, i64, i32, vp, i64, i64, i64, vp]
+    lib.lora_copy_padded.restype = ctypes.c_int
     lib.lora_workspace_errors.argtypes = [vp, vp, vp]
     lib.lora_workspace_errors.restype = ctypes.c_int
     lib.lora_status_string.argtypes = [ctypes.c_int]
@@ -425,3 +431,57 @@ def shrink_expand_noalloc(x, A, B, y, seg, out_offsets, *, scale=None, ranks=Non
                                             _ptr(errors_host), _stream(stream, dev))
     _check(st)
     return y
+
+
+def embedding_shrink(tok, A_emb, idx, *, scale=None, ranks=None, v=None, active=True, stream=None):
+    """v[t][k] = scale[s] * A_emb[s][tok[t]][k] for tokens with a valid slot and
+    an id inside the table (zero rows otherwise).  A_emb: [S, V, r_max] (the
+    adapters' A tables stacked transposed).  Returns v ([1, T, r_max] fp32)."""
+    if tok.dtype != torch.int32 or tok.dim() != 1 or idx.dtype != torch.int32 or idx.dim() != 1 \
+            or tok.numel() != idx.numel():
+        raise LoraError(LORA_ERR_INVALID_ARG, "tok and idx must be int32 tensors of T entries")
+    if A_emb.dim() != 3:
+        raise LoraError(LORA_ERR_INVALID_ARG, "A_emb must be [S, V, r_max]")
+    S, V, r_max = A_emb.shape
+    T = tok.numel()
+    dev = A_emb.device
+    if v is None:
+        v = torch.empty((1, T, r_max), dtype=torch.float32, device=dev)
+    if v.dtype != torch.float32 or not v.is_contiguous() or v.numel() != T * r_max:
+        raise LoraError(LORA_ERR_INVALID_ARG, "v must be contiguous float32 with T * r_max elements")
+    for name, t in (("tok", tok), ("idx", idx), ("A_emb", A_emb), ("v", v)):
+        _check_tensor(t, name, dev)
+    _check_slot_tables(dev, S, ranks, scale)
+    st = _load().lora_embedding_shrink(_dtype_code(A_emb), _ptr(tok), T, V, _ptr(A_emb), S, r_max,
+                                       _ptr(ranks), _ptr(scale), _ptr(idx), 1 if active else 0,
+                                       _ptr(v), _stream(stream, dev))
+    _check(st)
+    return v
+
+
+def embedding_apply(tok, A_emb, B_emb, y, seg, idx, *, scale=None, ranks=None, v=None, active=True,
+                    stream=None):
+    """The LoRA delta of an embedding layer: embedding_shrink, then the expand
+    y[t, :H] += B_emb[s] @ v[t] (B_emb: [S, H, r_max]).  seg is the batch's
+    segment record (from build_segments(idx, S)).  Returns (v, y)."""
+    v = embedding_shrink(tok, A_emb, idx, scale=scale, ranks=ranks, v=v, active=active, stream=stream)
+    expand(v, [B_emb], y, seg, [0], ranks=ranks, active=active, v_slice_stride=0, stream=stream)
+    return v, y
+
+
+def copy_padded(src, dst, *, transpose=False, stream=None):
+    """dst (a 2-D slot region, row-contiguous) = src (or src.T) in its top-left
+    corner, zeros elsewhere; src and dst on the same GPU, same dtype."""
+    if src.dtype != dst.dtype:
+        raise LoraError(LORA_ERR_INVALID_ARG, "src and dst must share a dtype")
+    if src.dim() != 2 or dst.dim() != 2 or src.stride(1) != 1 or dst.stride(1) != 1:
+        raise LoraError(LORA_ERR_INVALID_ARG, "src and dst must be 2-D with contiguous rows")
+    dev = dst.device
+    _check_rows(src, "src", dev)
+    _check_rows(dst, "dst", dev)
+    m_rows, m_cols = (src.shape[1], src.shape[0]) if transpose else (src.shape[0], src.shape[1])
+    st = _load().lora_copy_padded(_dtype_code(src), _ptr(src), m_rows, m_cols, max(src.stride(0), src.shape[1]),
+                                  1 if transpose else 0, _ptr(dst), dst.shape[0], dst.shape[1],
+                                  max(dst.stride(0), dst.shape[1]), _stream(stream, dev))
+    _check(st)
+    return dst

@@ -492,3 +492,51 @@ LORA_EXPORT lora_status lora_workspace_errors(const void* workspace, int32_t* ho
   if (e != hipSuccess) return hip_fail(e, "workspace error count copy");
   return LORA_OK;
 }
+
+LORA_EXPORT lora_status lora_embedding_shrink(lora_dtype dt, const int32_t* tok, int32_t T, int64_t V,
+                                              const void* A_emb, int32_t S, int32_t r_max, const int32_t* ranks,
+                                              const float* scale, const int32_t* idx, int32_t active_hint, float* v,
+                                              hipStream_t stream) {
+  clear_error();
+  if (!valid_dtype(dt)) return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", dt);
+  if (T < 0) return fail(LORA_ERR_INVALID_ARG, "T = %d is negative", T);
+  if (V < 1) return fail(LORA_ERR_INVALID_ARG, "V = %lld must be >= 1", (long long)V);
+  if (S < 1) return fail(LORA_ERR_INVALID_ARG, "S = %d must be >= 1", S);
+  if (S > LORA_MAX_SLOTS) return fail(LORA_ERR_UNSUPPORTED, "S = %d exceeds %d", S, LORA_MAX_SLOTS);
+  if (r_max < 1) return fail(LORA_ERR_INVALID_ARG, "r_max = %d must be >= 1", r_max);
+  if (r_max > LORA_MAX_RANK) return fail(LORA_ERR_UNSUPPORTED, "r_max = %d exceeds %d", r_max, LORA_MAX_RANK);
+  if (r_max % vec_of(dt))
+    return fail(LORA_ERR_UNSUPPORTED, "r_max = %d must be a multiple of %d for this dtype", r_max, vec_of(dt));
+  if (T == 0) return LORA_OK;
+  if (!tok || !idx || !A_emb || !v) return fail(LORA_ERR_INVALID_ARG, "tok, idx, A_emb or v is null");
+  if (!aligned16(A_emb) || !aligned16(v)) return fail(LORA_ERR_UNSUPPORTED, "A_emb and v must be 16-byte aligned");
+  if (V > ((int64_t)1 << 40) / ((int64_t)S * r_max)) return fail(LORA_ERR_UNSUPPORTED, "the stacked table is too large");
+  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
+  const hipError_t e = launch_embedding_shrink(dt, tok, idx, T, V, A_emb, S, r_max, ranks, scale, v, stream);
+  if (e != hipSuccess) return hip_fail(e, "embedding shrink launch");
+  return LORA_OK;
+}
+
+LORA_EXPORT lora_status lora_copy_padded(lora_dtype dt, const void* src, int64_t m_rows, int64_t m_cols, int64_t src_ld,
+                                         int32_t transpose, void* dst, int64_t dst_rows, int64_t dst_cols,
+                                         int64_t dst_ld, hipStream_t stream) {
+  clear_error();
+  if (!valid_dtype(dt)) return fail(LORA_ERR_INVALID_ARG, "unknown dtype %d", dt);
+  if (m_rows < 0 || m_cols < 0 || dst_rows < 0 || dst_cols < 0)
+    return fail(LORA_ERR_INVALID_ARG, "negative size");
+  if (m_rows > dst_rows || m_cols > dst_cols)
+    return fail(LORA_ERR_INVALID_ARG, "the matrix (%lld x %lld) does not fit the slot (%lld x %lld)",
+                (long long)m_rows, (long long)m_cols, (long long)dst_rows, (long long)dst_cols);
+  if (dst_ld < dst_cols) return fail(LORA_ERR_INVALID_ARG, "dst_ld is smaller than dst_cols");
+  if (m_rows > 0 && m_cols > 0) {
+    if (!src) return fail(LORA_ERR_INVALID_ARG, "src is null");
+    if (src_ld < (transpose ? m_rows : m_cols)) return fail(LORA_ERR_INVALID_ARG, "src_ld is too small");
+  }
+  if (dst_rows * dst_cols == 0) return LORA_OK;
+  if (!dst) return fail(LORA_ERR_INVALID_ARG, "dst is null");
+  const int esize = dt == LORA_F32 ? 4 : 2;
+  const hipError_t e = launch_copy_padded(esize, src, src_ld, transpose ? 1 : 0, m_rows, m_cols, dst, dst_rows,
+                                          dst_cols, dst_ld, stream);
+  if (e != hipSuccess) return hip_fail(e, "padded copy launch");
+  return LORA_OK;
+}

@@ -319,6 +319,19 @@ hipError_t launch_bgmv_expand(lora_dtype dt, const ExpandParams& p, bool tiles, 
 // launch (16-bit types only).
 hipError_t launch_mfma_expand(lora_dtype dt, const ExpandParams& p, bool groups, bool tiles, hipStream_t stream);
 
+// Shrink of an embedding adapter: v[t][k] = scale[s] * A_emb[s][tok[t]][k]
+// for every token (zero rows for tokens without a valid slot or id).
+hipError_t launch_embedding_shrink(lora_dtype dt, const int32_t* tok, const int32_t* idx, int32_t T, int64_t V,
+                                   const void* A_emb, int32_t S, int32_t r_max, const int32_t* ranks,
+                                   const float* scale, float* v, hipStream_t stream);
+
+// dst[i][j] = M[i][j] inside M's rows and columns, 0 elsewhere, for
+// i < dst_rows, j < dst_cols; M = src ([m_rows][m_cols], row stride src_ld)
+// or, with transpose, src^T (src then [m_cols][m_rows]).
+hipError_t launch_copy_padded(int elem_bytes, const void* src, int64_t src_ld, int transpose, int64_t m_rows,
+                              int64_t m_cols, void* dst, int64_t dst_rows, int64_t dst_cols, int64_t dst_ld,
+                              hipStream_t stream);
+
 // Workspace of the fused shrink-expand call.  The layout depends only on the
 // workspace's size: word 0 counts waits that gave up, the per-chunk counters
 // fill [counters, counters + counter_bytes), the producer slabs (or v, when

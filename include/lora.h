@@ -272,6 +272,57 @@ lora_status lora_shrink_expand(lora_dtype dt, const void *x, int64_t ldx, int32_
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Shrink of a LoRA on an embedding table ("Add multi-LoRA support",
+ * Features: adapters cover every linear layer and the embeddings, in PEFT
+ * format).  For token id w the layer's input is the one-hot vector e_w, so
+ * the shrink A_s e_w is column w of the adapter's r x V table A_s.  The
+ * tables are stacked transposed, one contiguous rank vector per vocabulary
+ * row:
+ *     v[t][k] = scale[s] * A_emb[s][tok[t]][k]            (k < r_s)
+ * for every token t with a valid slot s = idx[t] and 0 <= tok[t] < V; all
+ * other entries of v (rows of base-only tokens, of ids outside the table --
+ * such as tokens an adapter adds, which are looked up elsewhere -- and rank
+ * columns k >= r_s) are written as 0.  The embedding's delta is then
+ * lora_expand with one slice (B_emb [S][H][r_max], out_sizes = {H}) on v.
+ *   tok        [T] int32 device token ids
+ *   V          rows of the table (e.g. the vocabulary size)
+ *   A_emb      [S][V][r_max] device, 16-byte aligned, dtype dt
+ *   ranks, scale, active_hint   as lora_shrink
+ *   idx        [T] int32 device slots (-1 for base-only); read directly, no
+ *              segment record is needed
+ *   v          [T][r_max] fp32 device, 16-byte aligned, written in full when
+ *              the call runs
+ * One launch of T x 16 threads.  Errors: LORA_ERR_INVALID_ARG for a bad size
+ * or a null pointer, LORA_ERR_UNSUPPORTED for r_max outside the limits of
+ * lora_shrink or misaligned pointers; nothing is enqueued on an error.
+ */
+lora_status lora_embedding_shrink(lora_dtype dt, const int32_t *tok, int32_t T, int64_t V,
+                                  const void *A_emb, int32_t S, int32_t r_max, const int32_t *ranks,
+                                  const float *scale, const int32_t *idx, int32_t active_hint, float *v,
+                                  hipStream_t stream);
+
+/*
+ * Copy an adapter's matrix into its slot of a stacked tensor, zero-padded:
+ * the GPU tier of the adapter cache is a fixed number of slots, and adapters
+ * of different ranks share them ("Add multi-LoRA support", Features: tiered
+ * Disk -> CPU (LRU) -> GPU (fixed number of slots) cache; LoRAs with
+ * different ranks).  With M the source matrix (src, [m_rows][m_cols] with row
+ * stride src_ld) or, when transpose is non-zero, its transpose (src is then
+ * [m_cols][m_rows] with row stride src_ld):
+ *     dst[i][j] = (i < m_rows && j < m_cols) ? M[i][j] : 0
+ * for i < dst_rows and j < dst_cols, dst having row stride dst_ld.  For a
+ * linear layer's slot s: A_i[s] gets the adapter's [r][D] matrix (dst_rows =
+ * r_max, dst_cols = D), B_i[s] its [out][r] matrix (dst_cols = r_max); for an
+ * embedding the PEFT [r][V] table is copied transposed into A_emb[s]
+ * ([V][r_max]).  src and dst are device memory of dtype dt; the copy is
+ * stream-ordered.  LORA_ERR_INVALID_ARG for negative sizes, a matrix larger
+ * than the slot, a short stride or a null pointer.
+ */
+lora_status lora_copy_padded(lora_dtype dt, const void *src, int64_t m_rows, int64_t m_cols, int64_t src_ld,
+                             int32_t transpose, void *dst, int64_t dst_rows, int64_t dst_cols,
+                             int64_t dst_ld, hipStream_t stream);
+
+/*
  * lora_shrink_expand without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same arguments and result as lora_shrink_expand,

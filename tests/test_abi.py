@@ -374,3 +374,48 @@ def test_noalloc_rejects_on_the_host(kw, status):
     assert glsa.workspace_bytes(16384, 4, 8, 64) > glsa.NOALLOC_SCRATCH_BYTES
     assert _noalloc(**kw) == status
     assert glsa.lib().lora_last_error()
+
+
+# --------------------------------------------------------------------------
+# lora_embedding_shrink and lora_copy_padded: host-side checks (no GPU call)
+# --------------------------------------------------------------------------
+
+def _emb(**kw):
+    a = dict(dt=1, tok=FAKE, T=8, V=100, A=FAKE, S=4, r_max=16, ranks=None, scale=None, idx=FAKE,
+             active=1, v=FAKE)
+    a.update(kw)
+    return glsa.lib().lora_embedding_shrink(a["dt"], a["tok"], a["T"], a["V"], a["A"], a["S"], a["r_max"],
+                                            a["ranks"], a["scale"], a["idx"], a["active"], a["v"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=4), glsa.LORA_ERR_INVALID_ARG), (dict(T=-1), glsa.LORA_ERR_INVALID_ARG),
+    (dict(V=0), glsa.LORA_ERR_INVALID_ARG), (dict(S=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(S=2000), glsa.LORA_ERR_UNSUPPORTED), (dict(r_max=12), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(r_max=128), glsa.LORA_ERR_UNSUPPORTED), (dict(tok=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(idx=0), glsa.LORA_ERR_INVALID_ARG), (dict(v=0), glsa.LORA_ERR_INVALID_ARG),
+    (dict(A=FAKE + 4), glsa.LORA_ERR_UNSUPPORTED),
+])
+def test_embedding_shrink_rejects_bad_arguments(kw, status):
+    assert _emb(**kw) == status
+    assert glsa.lib().lora_last_error()
+
+
+def test_embedding_shrink_inactive_and_empty_are_host_side_no_ops():
+    assert _emb(active=0) == glsa.LORA_OK
+    assert _emb(T=0, tok=0, idx=0, v=0) == glsa.LORA_OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, FAKE, 4, 8, 8, 0, FAKE, 3, 8, 8), glsa.LORA_ERR_INVALID_ARG),    # more rows than the slot
+    ((1, FAKE, 4, 8, 8, 0, FAKE, 4, 6, 8), glsa.LORA_ERR_INVALID_ARG),    # more columns than the slot
+    ((1, FAKE, 4, 8, 4, 0, FAKE, 4, 8, 8), glsa.LORA_ERR_INVALID_ARG),    # short source stride
+    ((1, FAKE, 4, 8, 8, 0, FAKE, 4, 8, 4), glsa.LORA_ERR_INVALID_ARG),    # short slot stride
+    ((1, 0, 4, 8, 8, 0, FAKE, 4, 8, 8), glsa.LORA_ERR_INVALID_ARG),       # null source
+    ((1, FAKE, 4, 8, 8, 0, 0, 4, 8, 8), glsa.LORA_ERR_INVALID_ARG),       # null slot
+    ((9, FAKE, 4, 8, 8, 0, FAKE, 4, 8, 8), glsa.LORA_ERR_INVALID_ARG),    # dtype
+    ((1, FAKE, -1, 8, 8, 0, FAKE, 4, 8, 8), glsa.LORA_ERR_INVALID_ARG),   # negative size
+    ((1, FAKE, 8, 4, 4, 1, FAKE, 8, 4, 4), glsa.LORA_ERR_INVALID_ARG),    # transposed: stride < m_rows
+])
+def test_copy_padded_rejects_bad_arguments(args, status):
+    assert glsa.lib().lora_copy_padded(*args, None) == status
