@@ -573,6 +573,26 @@ def run_config(name, args, torch, glsa, dev, copy_gbs, headline):
                       traffic_ratio=round(traffic / dom["bytes"], 3) if traffic else None),
     )
 
+    # ---- the mask ("laning") form, where the stacked lanes allow it: the same
+    # layers with every token multiplied by all adapters' lanes, no segment
+    # build (compared with the gather step above, which includes its build)
+    if S * wl.r_max <= glsa.MASK_MAX_LANES and all(p.timed_expand for p in problems):
+        for st in sets:
+            for li, p in enumerate(problems):
+                d = st["layers"][li]
+                d["mws"] = glsa.alloc_mask_workspace(d["x"].dtype, T, p.D, S, p.n_slices, p.r_max, dev)
+
+        def do_mask(st):
+            for li, p in enumerate(problems):
+                d = st["layers"][li]
+                glsa.shrink_expand_mask(d["x"], d["A"], d["B"], d["y"], st["idx"], p.out_offsets,
+                                        workspace=d["mws"], scale=d["scale"], ranks=d["ranks"], v=d["v"])
+        mask_us = call_time_us(do_mask)
+        out["mask_form"] = dict(us=round(mask_us, 3), gather_step_us=out["step_us"],
+                                speedup_vs_gather=round(out["step_us"] / mask_us, 3),
+                                lanes=S * wl.r_max)
+        say(f"[bench] {name}: mask form {mask_us:.2f} us against the gather step {out['step_us']:.2f} us")
+
     # ---- checks of the timed output: set 0 restored, the step replayed once
     rows = check_rows(wl.idx, S)
     refs, seg_ref = oracle_refs(wl, rows)

@@ -17,6 +17,8 @@ Entry points (same names as the C ABI):
                                          the same without a workspace (allocates nothing)
     embedding_shrink(tok, A_emb, idx, ...) -> v of an embedding adapter ([1, T, r_max])
     embedding_apply(tok, A_emb, B_emb, y, seg, idx, ...) = embedding_shrink then expand
+    shrink_expand_mask(x, A, B, y, idx, out_offsets, workspace=...)
+                                         the mask ("laning") form for S * r_max <= 128
     alloc_workspace(T, S, n_slices, r_max, device) -> zeroed workspace for it
 """
 
@@ -94,6 +96,11 @@ def _load():
     lib.lora_embedding_shrink.restype = ctypes.c_int
     lib.lora_copy_padded.argtypes = [ctypes.c_int, vp, i64, i64, i64, i32, vp, i64, i64, i64, vp]
     lib.lora_copy_padded.restype = ctypes.c_int
+    lib.lora_mask_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32]
+    lib.lora_mask_workspace_bytes.restype = sz
+    lib.lora_shrink_expand_mask.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp, i32, i32,
+                                            vp, vp, vp, i32, vp, vp, i64, vp, sz, vp]
+    lib.lora_shrink_expand_mask.restype = ctypes.c_int
     lib.lora_workspace_errors.argtypes = [vp, vp, vp]
     lib.lora_workspace_errors.restype = ctypes.c_int
     lib.lora_status_string.argtypes = [ctypes.c_int]
@@ -352,7 +359,7 @@ def workspace_errors_async(ws, host_out, *, stream=None):
     return host_out
 
 
-def _shrink_expand_args(x, A, B, y, seg, out_offsets, scale, ranks, v, idx):
+def _shrink_expand_args(x, A, B, y, seg, out_offsets, scale, ranks, v, idx, record_bytes=None):
     """Checks and marshals the arguments shared by shrink_expand and
     shrink_expand_noalloc (everything before the workspace)."""
     A, B = list(A), list(B)
@@ -386,7 +393,8 @@ def _shrink_expand_args(x, A, B, y, seg, out_offsets, scale, ranks, v, idx):
     _check_tensor(v, "v", dev)
     _check_tensor(idx, "idx", dev)
     _check_slot_tables(dev, S, ranks, scale)
-    _check_record(seg, T, S, dev)
+    if record_bytes is None:
+        _check_record(seg, T, S, dev)
     n = len(A)
     a_ptrs = (ctypes.c_void_p * n)(*[a.data_ptr() for a in A])
     b_ptrs = (ctypes.c_void_p * n)(*[b.data_ptr() for b in B])
@@ -485,3 +493,38 @@ def copy_padded(src, dst, *, transpose=False, stream=None):
                                   max(dst.stride(0), dst.shape[1]), _stream(stream, dev))
     _check(st)
     return dst
+
+
+MASK_MAX_LANES = 128
+
+
+def mask_workspace_bytes(dtype, T, D, S, n_slices, r_max):
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_load().lora_mask_workspace_bytes(code, T, D, S, n_slices, r_max))
+
+
+def alloc_mask_workspace(dtype, T, D, S, n_slices, r_max, device):
+    n = mask_workspace_bytes(dtype, T, D, S, n_slices, r_max)
+    if n == 0:
+        raise LoraError(LORA_ERR_UNSUPPORTED, f"no mask form for S={S} r_max={r_max}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def shrink_expand_mask(x, A, B, y, idx, out_offsets, *, workspace, scale=None, ranks=None, v=None,
+                       active=True, stream=None):
+    """The mask form of shrink + expand: one dense product of every token tile
+    with all the stacked adapter lanes, each token keeping its own (S * r_max
+    <= 128).  Reads idx directly (no segment record).  Returns y."""
+    if idx.dtype != torch.int32 or idx.dim() != 1:
+        raise LoraError(LORA_ERR_INVALID_ARG, "idx must be a 1-D int32 tensor")
+    # (this form reads no segment record: the arguments are checked as for
+    # shrink_expand without one)
+    head, dev, ldy = _shrink_expand_args(x, A, B, y, None, out_offsets, scale, ranks, v, None,
+                                         record_bytes=0)
+    _check_tensor(idx, "idx", dev, min_numel=head[3])
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise LoraError(LORA_ERR_INVALID_ARG, "workspace must be a contiguous uint8 tensor")
+    st = _load().lora_shrink_expand_mask(*head[:14], _ptr(idx), 1 if active else 0, _ptr(v), _ptr(y), ldy,
+                                         _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st)
+    return y

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblora_mi355x.so")
-SOURCES = ["api.hip", "segments.hip", "shrink.hip", "bgmv.hip", "sgmv.hip", "fused.hip", "embedding.hip", "slots.hip"]
+SOURCES = ["api.hip", "segments.hip", "shrink.hip", "bgmv.hip", "sgmv.hip", "fused.hip", "embedding.hip", "slots.hip", "mask.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

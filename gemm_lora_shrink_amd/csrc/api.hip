@@ -540,3 +540,49 @@ LORA_EXPORT lora_status lora_copy_padded(lora_dtype dt, const void* src, int64_t
   if (e != hipSuccess) return hip_fail(e, "padded copy launch");
   return LORA_OK;
 }
+
+LORA_EXPORT size_t lora_mask_workspace_bytes(lora_dtype dt, int32_t T, int32_t D, int32_t S, int32_t n_slices,
+                                             int32_t r_max) {
+  if (!valid_dtype(dt) || T < 0 || D < 1 || S < 1 || n_slices < 1 || n_slices > LORA_MAX_SLICES || r_max < 1 ||
+      (int64_t)S * r_max > kMaskMaxLanes)
+    return 0;
+  const int64_t b = mask_need_bytes(dt, T, D, S, n_slices, r_max);
+  return (size_t)((b + 255) & ~int64_t(255));
+}
+
+LORA_EXPORT lora_status lora_shrink_expand_mask(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D,
+                                                int32_t n_slices, const void* const* A, const void* const* B,
+                                                const int64_t* out_sizes, const int64_t* out_offsets, int32_t S,
+                                                int32_t r_max, const int32_t* ranks, const float* scale,
+                                                const int32_t* idx, int32_t active_hint, float* v, void* y,
+                                                int64_t ldy, void* workspace, size_t workspace_bytes,
+                                                hipStream_t stream) {
+  clear_error();
+  // the checks shared with lora_shrink and lora_expand; this form reads no
+  // segment record, so the workspace (256-byte aligned as a record must be)
+  // stands in for it there, and for v when the caller passes none
+  if (!workspace) return fail(LORA_ERR_INVALID_ARG, "workspace is null");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(LORA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  float* v_chk = v ? v : static_cast<float*>(workspace);
+  ShrinkParams sp;
+  lora_status st = prep_shrink(dt, x, ldx, T, D, n_slices, A, S, r_max, ranks, scale, workspace, v_chk, sp);
+  if (st != LORA_OK) return st;
+  ExpandParams ep;
+  st = prep_expand(dt, v_chk, (int64_t)T * r_max, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks,
+                   workspace, y, ldy, ep);
+  if (st != LORA_OK) return st;
+  if ((int64_t)S * r_max > kMaskMaxLanes)
+    return fail(LORA_ERR_UNSUPPORTED, "S * r_max = %lld exceeds the %d lanes of the mask form",
+                (long long)S * r_max, kMaskMaxLanes);
+  if (T == 0) return LORA_OK;
+  if (!idx) return fail(LORA_ERR_INVALID_ARG, "idx is null");
+  const int64_t need = mask_need_bytes(dt, T, D, S, n_slices, r_max);
+  if ((int64_t)workspace_bytes < need)
+    return fail(LORA_ERR_INVALID_ARG, "workspace has %zu bytes, the call needs %lld", workspace_bytes,
+                (long long)need);
+  if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
+  const hipError_t e = launch_mask(dt, sp, ep, idx, static_cast<float*>(workspace), v, stream);
+  if (e != hipSuccess) return hip_fail(e, "mask shrink-expand launch");
+  return LORA_OK;
+}

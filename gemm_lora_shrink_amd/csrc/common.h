@@ -18,6 +18,7 @@ constexpr int kTile = 64;   // tokens per segmented (SGMV) work item
 constexpr int kSgmvMinTokens = 48;  // AUTO: slots with this many tokens go to SGMV
 constexpr int kFusedMaxTokens = 4096;  // lora_shrink_expand runs as one launch up to this T
 constexpr int kFusedBuildMaxSlots = 256;  // ... and builds the record inside that launch up to this S
+constexpr int kMaskMaxLanes = 128;  // the mask form takes adapters of at most this many stacked ranks (S * r_max)
 
 enum InfoWord {
   kNumActive = 0,
@@ -331,6 +332,15 @@ hipError_t launch_embedding_shrink(lora_dtype dt, const int32_t* tok, const int3
 hipError_t launch_copy_padded(int elem_bytes, const void* src, int64_t src_ld, int transpose, int64_t m_rows,
                               int64_t m_cols, void* dst, int64_t dst_rows, int64_t dst_cols, int64_t dst_ld,
                               hipStream_t stream);
+
+// Mask form of shrink + expand (S * r_max <= kMaskMaxLanes): the stacked
+// rank lanes, the shrink's K parts and the workspace bytes it needs
+// ([n_slices][parts][T][lanes] fp32 partial sums).
+int32_t mask_lanes(lora_dtype dt, int32_t S, int32_t r_max);
+int32_t mask_parts(int32_t T, int32_t D, int32_t n_slices);
+int64_t mask_need_bytes(lora_dtype dt, int32_t T, int32_t D, int32_t S, int32_t n_slices, int32_t r_max);
+hipError_t launch_mask(lora_dtype dt, const ShrinkParams& sp, const ExpandParams& ep, const int32_t* idx,
+                       float* part, float* v, hipStream_t stream);
 
 // Workspace of the fused shrink-expand call.  The layout depends only on the
 // workspace's size: word 0 counts waits that gave up, the per-chunk counters
