@@ -75,6 +75,8 @@ def parse():
                     help="build the segment record with lora_build_segments before the first layer "
                          "instead of inside the first layer's shrink_expand call")
     ap.add_argument("--eager", action="store_true", help="time host launches instead of graph replay")
+    ap.add_argument("--b-layout", default="auto", choices=["auto", "padded", "rank_rows"],
+                    help="storage of the slots' B rows; auto: rank_rows for workloads with per-slot ranks")
     ap.add_argument("--path", default="fused", choices=["fused", "split"],
                     help="fused: each layer with a timed expand is one shrink_expand call; "
                          "split: a shrink call then an expand call")
@@ -387,6 +389,16 @@ def run_config(name, args, torch, glsa, dev, copy_gbs, headline):
                      and S <= 256)
 
     base = [problem_to_device(p, dev) for p in problems]
+    # adapters of per-slot ranks are stored rank-compact (each slot's B rows
+    # packed with the stride of its rank): an adapter-load-time layout, so
+    # that low-rank slots are read without their zero padding
+    b_layout = "rank_rows" if args.b_layout == "auto" and problems[0].ranks is not None else \
+        ("padded" if args.b_layout == "auto" else args.b_layout)
+    if b_layout == "rank_rows":
+        for p, d in zip(problems, base):
+            rk = p.ranks if p.ranks is not None else [p.r_max] * p.S
+            d["B"] = [glsa.pack_b_rank_rows(b, rk) for b in d["B"]]
+        torch.cuda.synchronize()
 
     def nbytes(d):
         tot = d["x"].numel() * d["x"].element_size() + d["y"].numel() * d["y"].element_size()
@@ -420,13 +432,14 @@ def run_config(name, args, torch, glsa, dev, copy_gbs, headline):
     def do_expand(st, li):
         d, p = st["layers"][li], problems[li]
         glsa.expand(d["v"], d["B"], d["y"], st["seg"], p.out_offsets, ranks=d["ranks"],
-                    active=active)
+                    active=active, b_layout=b_layout)
 
     def do_fused(st, li):
         d, p = st["layers"][li], problems[li]
         glsa.shrink_expand(d["x"], d["A"], d["B"], d["y"], st["seg"], p.out_offsets,
                            workspace=d["ws"], scale=d["scale"], ranks=d["ranks"], v=d["v"],
-                           idx=st["idx"] if build_in_call and li == 0 else None, active=active)
+                           idx=st["idx"] if build_in_call and li == 0 else None, active=active,
+                           b_layout=b_layout)
 
     def step(st):
         # a base-only batch: the host knows no adapter is active and runs
@@ -451,7 +464,7 @@ def run_config(name, args, torch, glsa, dev, copy_gbs, headline):
 
     say(f"[bench] {name}: T={T} S={S} dtype={wl.dtype} sets={n_sets} x {set_bytes / 1e6:.1f} MB, "
         f"setup {time.perf_counter() - t_setup:.1f} s")
-    out = dict(title=cfg["title"], T=T, S=S, dtype=wl.dtype, input_sets=n_sets,
+    out = dict(title=cfg["title"], T=T, S=S, dtype=wl.dtype, b_layout=b_layout, input_sets=n_sets,
                input_set_bytes=set_bytes, rotated_bytes=n_sets * set_bytes)
 
     if not active:
@@ -576,7 +589,7 @@ def run_config(name, args, torch, glsa, dev, copy_gbs, headline):
     # ---- the mask ("laning") form, where the stacked lanes allow it: the same
     # layers with every token multiplied by all adapters' lanes, no segment
     # build (compared with the gather step above, which includes its build)
-    if S * wl.r_max <= glsa.MASK_MAX_LANES and all(p.timed_expand for p in problems):
+    if S * wl.r_max <= glsa.MASK_MAX_LANES and all(p.timed_expand for p in problems) and b_layout == "padded":
         for st in sets:
             for li, p in enumerate(problems):
                 d = st["layers"][li]

@@ -37,6 +37,8 @@ LORA_ERR_INDEX = 3
 LORA_ERR_HIP = 4
 
 MODES = {"auto": 0, "bgmv": 1, "sgmv": 2}
+# lora_b_layout: how each slot's B rows are stored in its [out][r_max] region
+B_LAYOUTS = {"padded": 0, "rank_rows": 1}
 # LORA_NOALLOC_SCRATCH_BYTES of include/lora.h: the per-device scratch of
 # shrink_expand_noalloc
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -79,7 +81,7 @@ def _load():
     lib.lora_shrink.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, i32, i32, vp, vp, vp,
                                 i32, vp, vp]
     lib.lora_shrink.restype = ctypes.c_int
-    lib.lora_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, vp, vp, vp, i32, i32, vp, vp,
+    lib.lora_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, vp, vp, vp, i32, i32, vp, i32, vp,
                                 i32, vp, i64, vp]
     lib.lora_expand.restype = ctypes.c_int
     lib.lora_fused_max_tokens.argtypes = []
@@ -87,10 +89,10 @@ def _load():
     lib.lora_shrink_expand_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.lora_shrink_expand_workspace_bytes.restype = sz
     lib.lora_shrink_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp, i32,
-                                       i32, vp, vp, vp, vp, i32, vp, vp, i64, vp, sz, vp]
+                                       i32, vp, i32, vp, vp, vp, i32, vp, vp, i64, vp, sz, vp]
     lib.lora_shrink_expand.restype = ctypes.c_int
     lib.lora_shrink_expand_noalloc.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp,
-                                               i32, i32, vp, vp, vp, vp, i32, vp, vp, i64, vp, vp]
+                                               i32, i32, vp, i32, vp, vp, vp, i32, vp, vp, i64, vp, vp]
     lib.lora_shrink_expand_noalloc.restype = ctypes.c_int
     lib.lora_embedding_shrink.argtypes = [ctypes.c_int, vp, i32, i64, vp, i32, i32, vp, vp, vp, i32, vp, vp]
     lib.lora_embedding_shrink.restype = ctypes.c_int
@@ -279,8 +281,15 @@ def shrink(x, A, seg, *, scale=None, ranks=None, v=None, active=True, stream=Non
     return v
 
 
+def _b_layout(b_layout):
+    try:
+        return B_LAYOUTS[b_layout]
+    except KeyError:
+        raise LoraError(LORA_ERR_INVALID_ARG, f"unknown B layout {b_layout!r}") from None
+
+
 def expand(v, B, y, seg, out_offsets, *, ranks=None, active=True, v_slice_stride=None,
-           stream=None):
+           b_layout="padded", stream=None):
     """y[t, off_i:off_i+out_i] += B_i[s] @ v[i][t] for active tokens (in place)."""
     B = list(B)
     if not B or len(B) > MAX_SLICES:
@@ -310,17 +319,17 @@ def expand(v, B, y, seg, out_offsets, *, ranks=None, active=True, v_slice_stride
     sizes = (ctypes.c_int64 * n)(*[b.shape[1] for b in B])
     offs = (ctypes.c_int64 * n)(*[int(o) for o in out_offsets])
     st = _load().lora_expand(_dtype_code(y), _ptr(v), v_slice_stride, T, n, ptrs, sizes, offs,
-                             S, r_max, _ptr(ranks), _ptr(seg), 1 if active else 0, _ptr(y), ldy,
-                             _stream(stream, y.device))
+                             S, r_max, _ptr(ranks), _b_layout(b_layout), _ptr(seg), 1 if active else 0,
+                             _ptr(y), ldy, _stream(stream, y.device))
     _check(st)
     return y
 
 
 def apply(x, A, B, y, seg, out_offsets, *, scale=None, ranks=None, v=None, active=True,
-          stream=None):
+          b_layout="padded", stream=None):
     """Shrink then expand; returns (v, y)."""
     v = shrink(x, A, seg, scale=scale, ranks=ranks, v=v, active=active, stream=stream)
-    expand(v, B, y, seg, out_offsets, ranks=ranks, active=active, stream=stream)
+    expand(v, B, y, seg, out_offsets, ranks=ranks, active=active, b_layout=b_layout, stream=stream)
     return v, y
 
 
@@ -405,7 +414,7 @@ def _shrink_expand_args(x, A, B, y, seg, out_offsets, scale, ranks, v, idx, reco
 
 
 def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=None, v=None,
-                  idx=None, active=True, stream=None):
+                  idx=None, active=True, b_layout="padded", stream=None):
     """Shrink then expand in one call; y updated in place.  Returns y.
 
     v (optional, [n_slices, T, r_max] float32) receives the intermediate.
@@ -418,14 +427,14 @@ def shrink_expand(x, A, B, y, seg, out_offsets, *, workspace, scale=None, ranks=
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise LoraError(LORA_ERR_INVALID_ARG, "workspace must be a contiguous uint8 tensor")
     _check_tensor(workspace, "workspace", dev)
-    st = _load().lora_shrink_expand(*head, 1 if active else 0, _ptr(v), _ptr(y), ldy,
-                                    _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    st = _load().lora_shrink_expand(*head[:13], _b_layout(b_layout), *head[13:], 1 if active else 0, _ptr(v),
+                                    _ptr(y), ldy, _ptr(workspace), workspace.numel(), _stream(stream, dev))
     _check(st)
     return y
 
 
 def shrink_expand_noalloc(x, A, B, y, seg, out_offsets, *, scale=None, ranks=None, v=None,
-                          idx=None, active=True, errors_host=None, stream=None):
+                          idx=None, active=True, errors_host=None, b_layout="padded", stream=None):
     """shrink_expand without a workspace: the library's per-device scratch of
     NOALLOC_SCRATCH_BYTES bytes stands in for it, and the call allocates
     nothing.  Calls that may overlap on one device race.  errors_host
@@ -435,8 +444,8 @@ def shrink_expand_noalloc(x, A, B, y, seg, out_offsets, *, scale=None, ranks=Non
     if errors_host is not None and (errors_host.device.type != "cpu" or not errors_host.is_pinned()
                                     or errors_host.dtype != torch.int32):
         raise LoraError(LORA_ERR_INVALID_ARG, "errors_host must be a pinned int32 host tensor")
-    st = _load().lora_shrink_expand_noalloc(*head, 1 if active else 0, _ptr(v), _ptr(y), ldy,
-                                            _ptr(errors_host), _stream(stream, dev))
+    st = _load().lora_shrink_expand_noalloc(*head[:13], _b_layout(b_layout), *head[13:], 1 if active else 0,
+                                            _ptr(v), _ptr(y), ldy, _ptr(errors_host), _stream(stream, dev))
     _check(st)
     return y
 
@@ -528,3 +537,21 @@ def shrink_expand_mask(x, A, B, y, idx, out_offsets, *, workspace, scale=None, r
                                          _ptr(workspace), workspace.numel(), _stream(stream, dev))
     _check(st)
     return y
+
+
+def pack_b_rank_rows(B, ranks_host, *, stream=None):
+    """A copy of a stacked B ([S, out, r_max], padded layout) in the rank-rows
+    layout: slot s's rows packed with stride roundup(ranks_host[s], 8) (16-bit)
+    or roundup(.., 4) (fp32) from the start of its region, zeros between the
+    rank and the stride.  Each slot is placed with the library's
+    lora_copy_padded; this is adapter-load-time work, not part of a step."""
+    S, out, r_max = B.shape
+    unit = 4 if B.dtype == torch.float32 else 8
+    packed = torch.zeros_like(B)
+    for s_ in range(S):
+        r = max(0, min(int(ranks_host[s_]), r_max))
+        ld = max(unit, -(-r // unit) * unit) if r else unit
+        ld = min(ld, r_max)
+        dst = packed[s_].view(-1)[:out * ld].view(out, ld)
+        copy_padded(B[s_][:, :r] if r else B[s_][:, :0], dst, stream=stream)
+    return packed

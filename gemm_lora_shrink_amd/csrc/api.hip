@@ -228,10 +228,12 @@ lora_status prep_shrink(lora_dtype dt, const void* x, int64_t ldx, int32_t T, in
 // Host checks of the expand arguments; fills p.
 lora_status prep_expand(lora_dtype dt, const float* v, int64_t v_slice_stride, int32_t T, int32_t n_slices,
                         const void* const* B, const int64_t* out_sizes, const int64_t* out_offsets, int32_t S,
-                        int32_t r_max, const int32_t* ranks, const void* seg, void* y, int64_t ldy,
-                        ExpandParams& p) {
+                        int32_t r_max, const int32_t* ranks, int32_t b_layout, const void* seg, void* y,
+                        int64_t ldy, ExpandParams& p) {
   lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
   if (st != LORA_OK) return st;
+  if (b_layout != LORA_B_PADDED && b_layout != LORA_B_RANK_ROWS)
+    return fail(LORA_ERR_INVALID_ARG, "unknown B layout %d", b_layout);
   const int vec = vec_of(dt);
   if (T == 0) return LORA_OK;  // empty batch: nothing to read or write
   if (!v || !y) return fail(LORA_ERR_INVALID_ARG, "v or y is null");
@@ -272,6 +274,7 @@ lora_status prep_expand(lora_dtype dt, const float* v, int64_t v_slice_stride, i
   p.r_max = r_max;
   p.n_slices = n_slices;
   p.T = T;
+  p.b_row_unit = b_layout == LORA_B_RANK_ROWS ? vec : 0;
   return LORA_OK;
 }
 
@@ -312,12 +315,12 @@ LORA_EXPORT lora_status lora_shrink(lora_dtype dt, const void* x, int64_t ldx, i
 LORA_EXPORT lora_status lora_expand(lora_dtype dt, const float* v, int64_t v_slice_stride, int32_t T,
                                     int32_t n_slices, const void* const* B, const int64_t* out_sizes,
                                     const int64_t* out_offsets, int32_t S, int32_t r_max, const int32_t* ranks,
-                                    const void* seg, int32_t active_hint, void* y, int64_t ldy,
+                                    int32_t b_layout, const void* seg, int32_t active_hint, void* y, int64_t ldy,
                                     hipStream_t stream) {
   clear_error();
   ExpandParams p;
-  const lora_status st =
-      prep_expand(dt, v, v_slice_stride, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks, seg, y, ldy, p);
+  const lora_status st = prep_expand(dt, v, v_slice_stride, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks,
+                                     b_layout, seg, y, ldy, p);
   if (st != LORA_OK || T == 0) return st;
   if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
   const hipError_t e = run_expand(dt, p, stream);
@@ -342,9 +345,9 @@ namespace {
 lora_status shrink_expand_impl(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D, int32_t n_slices,
                                const void* const* A, const void* const* B, const int64_t* out_sizes,
                                const int64_t* out_offsets, int32_t S, int32_t r_max, const int32_t* ranks,
-                               const float* scale, const void* seg, const int32_t* idx, int32_t active_hint, float* v,
-                               void* y, int64_t ldy, char* ws, int64_t ws_bytes, bool clear_first,
-                               bool* ran, hipStream_t stream) {
+                               int32_t b_layout, const float* scale, const void* seg, const int32_t* idx,
+                               int32_t active_hint, float* v, void* y, int64_t ldy, char* ws, int64_t ws_bytes,
+                               bool clear_first, bool* ran, hipStream_t stream) {
   *ran = false;
   // without a caller v, the two-launch form keeps v in the workspace's data
   // region (never in the header or the counters)
@@ -354,8 +357,8 @@ lora_status shrink_expand_impl(lora_dtype dt, const void* x, int64_t ldx, int32_
   lora_status st = prep_shrink(dt, x, ldx, T, D, n_slices, A, S, r_max, ranks, scale, seg, v_eff, sp);
   if (st != LORA_OK) return st;
   ExpandParams ep;
-  st = prep_expand(dt, v_eff, (int64_t)T * r_max, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks, seg, y,
-                   ldy, ep);
+  st = prep_expand(dt, v_eff, (int64_t)T * r_max, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks, b_layout,
+                   seg, y, ldy, ep);
   if (st != LORA_OK || T == 0) return st;
   if (active_hint == 0) return LORA_OK;  // base-only batch: nothing is enqueued
   hipError_t e = hipSuccess;
@@ -406,9 +409,9 @@ std::vector<ScratchOfDevice> g_scratch;
 LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D,
                                            int32_t n_slices, const void* const* A, const void* const* B,
                                            const int64_t* out_sizes, const int64_t* out_offsets, int32_t S,
-                                           int32_t r_max, const int32_t* ranks, const float* scale, const void* seg,
-                                           const int32_t* idx, int32_t active_hint, float* v, void* y, int64_t ldy,
-                                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                           int32_t r_max, const int32_t* ranks, int32_t b_layout, const float* scale,
+                                           const void* seg, const int32_t* idx, int32_t active_hint, float* v, void* y,
+                                           int64_t ldy, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
   if (st != LORA_OK) return st;
@@ -420,17 +423,18 @@ LORA_EXPORT lora_status lora_shrink_expand(lora_dtype dt, const void* x, int64_t
     return fail(LORA_ERR_INVALID_ARG, "workspace has %zu bytes, the call needs %lld", workspace_bytes,
                 (long long)need);
   bool ran;
-  return shrink_expand_impl(dt, x, ldx, T, D, n_slices, A, B, out_sizes, out_offsets, S, r_max, ranks, scale, seg,
-                            idx, active_hint, v, y, ldy, static_cast<char*>(workspace), (int64_t)workspace_bytes,
-                            /*clear_first=*/false, &ran, stream);
+  return shrink_expand_impl(dt, x, ldx, T, D, n_slices, A, B, out_sizes, out_offsets, S, r_max, ranks, b_layout,
+                            scale, seg, idx, active_hint, v, y, ldy, static_cast<char*>(workspace),
+                            (int64_t)workspace_bytes, /*clear_first=*/false, &ran, stream);
 }
 
 LORA_EXPORT lora_status lora_shrink_expand_noalloc(lora_dtype dt, const void* x, int64_t ldx, int32_t T, int32_t D,
                                                    int32_t n_slices, const void* const* A, const void* const* B,
                                                    const int64_t* out_sizes, const int64_t* out_offsets, int32_t S,
-                                                   int32_t r_max, const int32_t* ranks, const float* scale,
-                                                   const void* seg, const int32_t* idx, int32_t active_hint, float* v,
-                                                   void* y, int64_t ldy, int32_t* errors_host, hipStream_t stream) {
+                                                   int32_t r_max, const int32_t* ranks, int32_t b_layout,
+                                                   const float* scale, const void* seg, const int32_t* idx,
+                                                   int32_t active_hint, float* v, void* y, int64_t ldy,
+                                                   int32_t* errors_host, hipStream_t stream) {
   clear_error();
   lora_status st = check_common(dt, T, n_slices, S, r_max, seg);
   if (st != LORA_OK) return st;
@@ -470,8 +474,9 @@ LORA_EXPORT lora_status lora_shrink_expand_noalloc(lora_dtype dt, const void* x,
   e = hipStreamIsCapturing(stream, &cap);
   if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
   bool ran = false;
-  st = shrink_expand_impl(dt, x, ldx, T, D, n_slices, A, B, out_sizes, out_offsets, S, r_max, ranks, scale, seg, idx,
-                          active_hint, v, y, ldy, ptr, (int64_t)LORA_NOALLOC_SCRATCH_BYTES, !cleared, &ran, stream);
+  st = shrink_expand_impl(dt, x, ldx, T, D, n_slices, A, B, out_sizes, out_offsets, S, r_max, ranks, b_layout, scale,
+                          seg, idx, active_hint, v, y, ldy, ptr, (int64_t)LORA_NOALLOC_SCRATCH_BYTES, !cleared, &ran,
+                          stream);
   if (ran && !cleared && cap == hipStreamCaptureStatusNone) {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     for (ScratchOfDevice& sd : g_scratch)
@@ -570,7 +575,7 @@ LORA_EXPORT lora_status lora_shrink_expand_mask(lora_dtype dt, const void* x, in
   if (st != LORA_OK) return st;
   ExpandParams ep;
   st = prep_expand(dt, v_chk, (int64_t)T * r_max, T, n_slices, B, out_sizes, out_offsets, S, r_max, ranks,
-                   workspace, y, ldy, ep);
+                   LORA_B_PADDED, workspace, y, ldy, ep);
   if (st != LORA_OK) return st;
   if ((int64_t)S * r_max > kMaskMaxLanes)
     return fail(LORA_ERR_UNSUPPORTED, "S * r_max = %lld exceeds the %d lanes of the mask form",

@@ -114,7 +114,8 @@ __global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(ExpandParams p, i
 
   const int j = j0 + tid * kColsPerLane;
   if (j < out) {
-  const Elem* Bb = reinterpret_cast<const Elem*>(p.B[slice]) + ((int64_t)s * out + j) * p.r_max;
+  const int ldb = b_row_stride(p, r);
+  const Elem* Bb = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max + (int64_t)j * ldb;
   Elem* yb = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + j;
   // the group's y values are loaded before any store, so the loads of all
   // tokens are in flight together
@@ -133,11 +134,11 @@ __global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(ExpandParams p, i
     float bf[kColsPerLane][kKChunk];
 #pragma unroll
     for (int c = 0; c < kColsPerLane; ++c) {
-      const Elem* row = Bb + (int64_t)c * p.r_max + k0;
+      const Elem* row = Bb + (int64_t)c * ldb + k0;
       if constexpr (sizeof(Elem) == 4) {
         // 8 fp32 values = two 16-byte loads; r_max is a multiple of 4
         u32x4 lo = ld16(row);
-        u32x4 hi = (k0 + 4 < p.r_max) ? ld16(row + 4) : u32x4{0, 0, 0, 0};
+        u32x4 hi = (k0 + 4 < ldb) ? ld16(row + 4) : u32x4{0, 0, 0, 0};
         Tr::to_float(lo, &bf[c][0]);
         Tr::to_float(hi, &bf[c][4]);
       } else {

@@ -235,7 +235,15 @@ struct ExpandParams {
   void* y;
   int64_t ldy;
   int32_t S, r_max, n_slices, T;
+  int32_t b_row_unit;  // 0: B rows of r_max elements; else rows of the slot's rank rounded up to this
 };
+
+// Elements between consecutive rows j, j + 1 of one slot's B (rank r): r_max
+// in the padded layout, the rank rounded up to whole 16-byte pieces in the
+// rank-rows layout (the slot's region keeps its [out][r_max] size either way).
+__device__ inline int b_row_stride(const ExpandParams& p, int r) {
+  return p.b_row_unit ? (r + p.b_row_unit - 1) / p.b_row_unit * p.b_row_unit : p.r_max;
+}
 
 // Persistent work loops.  A launch has a fixed number of workgroups (a
 // multiple of 8, sized to what the chip holds at once) and walks a work list

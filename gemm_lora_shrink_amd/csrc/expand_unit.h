@@ -75,6 +75,7 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const VSrc& vs
   const int nks = r > 32 ? 2 : 1;
   const bool ragged_rank = (r & 7) != 0;
   const Elem* Bs = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max;
+  const int ldb = b_row_stride(p, r);
   const Elem* yzero = reinterpret_cast<const Elem*>(g_zero16);
   Elem* ybase = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + yc;
 
@@ -92,7 +93,7 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const VSrc& vs
       for (int ks = 0; ks < 2; ++ks) {
         const int k0 = ks * 32 + kg * 8;
         const bool ok = ct < ct_end && ks < nks && row < out && k0 < r;
-        bd[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok);
+        bd[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * ldb + k0 : 0), ok);
       }
     }
   };

@@ -53,6 +53,7 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
   const int nks = r > 32 ? 2 : 1;  // 32-wide rank steps
   const bool ragged_rank = (r & 7) != 0;
   const Elem* Bs = reinterpret_cast<const Elem*>(p.B[slice]) + (int64_t)s * out * p.r_max;
+  const int ldb = b_row_stride(p, r);
   Elem* ybase = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + yc;
 
   // this thread's v row: token tid / 4, ranks 16 (tid % 4) .. +15
@@ -94,7 +95,7 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
       for (int ks = 0; ks < 2; ++ks) {
         const int k0 = ks * 32 + kg * 8;
         const bool ok = ct < ct_end && ks < nks && row < out && k0 < r;
-        bop[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * p.r_max + k0 : 0), ok);
+        bop[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * ldb + k0 : 0), ok);
       }
     }
   };

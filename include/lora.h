@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 1
+#define LORA_ABI_VERSION 2
 
 /* Largest supported rank ("Add multi-LoRA support", Limitations). */
 #define LORA_MAX_RANK 64
@@ -75,6 +75,20 @@ typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
  *   SGMV: every slot in tiles of at most 64 tokens.
  * fp32 data always runs on the gather kernels, whatever the mode. */
 typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode;
+
+/* How the rows of one slot's B are stored inside the slot's [out_i][r_max]
+ * region of a stacked B_i [S][out_i][r_max] ("Add multi-LoRA support",
+ * Features: adapters of different ranks, to be made more performant).
+ *   PADDED:    row j of slot s at element j * r_max of the region, columns
+ *              k >= r_s being padding.
+ *   RANK_ROWS: the rows packed with stride roundup(r_s, 8) (fp16/bf16) or
+ *              roundup(r_s, 4) (fp32) elements from the start of the region,
+ *              so that a slot of low rank is read without its padding: row j at
+ *              element j * roundup(r_s, ...) of the region; what lies past the
+ *              packed rows is never read.  Entries between r_s and the rounded
+ *              stride are ignored.  lora_copy_padded places an adapter this way
+ *              when given that stride as dst_ld (see lora_copy_padded). */
+typedef enum { LORA_B_PADDED = 0, LORA_B_RANK_ROWS = 1 } lora_b_layout;
 
 /* ------------------------------------------------------------------------ */
 /* Segment record                                                           */
@@ -160,6 +174,8 @@ lora_status lora_build_segments(const int32_t *idx, int32_t T, int32_t S, int32_
  *   ranks       [S] int32 device, nullable (= r_max for every slot); only rank
  *               rows/columns k < ranks[s] take part; values are clamped to
  *               [0, r_max]
+ *   b_layout    (expand calls) a lora_b_layout: how each slot's B rows are
+ *               stored in its region
  *   seg         the record lora_build_segments wrote for this batch's idx
  *   active_hint 0 when the caller knows that no token of the batch has a valid
  *               slot: the call then returns LORA_OK having enqueued nothing, so
@@ -201,12 +217,12 @@ lora_status lora_shrink(lora_dtype dt, const void *x, int64_t ldx, int32_t T, in
 lora_status lora_expand(lora_dtype dt, const float *v, int64_t v_slice_stride, int32_t T,
                         int32_t n_slices, const void *const *B, const int64_t *out_sizes,
                         const int64_t *out_offsets, int32_t S, int32_t r_max,
-                        const int32_t *ranks, const void *seg, int32_t active_hint, void *y,
-                        int64_t ldy, hipStream_t stream);
+                        const int32_t *ranks, int32_t b_layout, const void *seg, int32_t active_hint,
+                        void *y, int64_t ldy, hipStream_t stream);
 
 /*
  * Shrink then expand of one layer in a single call: the result of lora_shrink
- * followed by lora_expand with v_slice_stride = T * r_max (the shrink and
+ * followed by lora_expand (with the same b_layout) with v_slice_stride = T * r_max (the shrink and
  * expand of "Add multi-LoRA support", with the fp32 intermediate its
  * Limitations ask for), for decode-shaped batches whose layers are dominated
  * by launch and memory latency rather than by bytes.
@@ -266,9 +282,9 @@ int32_t lora_fused_max_tokens(void);
 lora_status lora_shrink_expand(lora_dtype dt, const void *x, int64_t ldx, int32_t T, int32_t D,
                                int32_t n_slices, const void *const *A, const void *const *B,
                                const int64_t *out_sizes, const int64_t *out_offsets, int32_t S,
-                               int32_t r_max, const int32_t *ranks, const float *scale,
-                               const void *seg, const int32_t *idx, int32_t active_hint,
-                               float *v, void *y, int64_t ldy, void *workspace,
+                               int32_t r_max, const int32_t *ranks, int32_t b_layout,
+                               const float *scale, const void *seg, const int32_t *idx,
+                               int32_t active_hint, float *v, void *y, int64_t ldy, void *workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -354,9 +370,45 @@ lora_status lora_copy_padded(lora_dtype dt, const void *src, int64_t m_rows, int
 lora_status lora_shrink_expand_noalloc(lora_dtype dt, const void *x, int64_t ldx, int32_t T, int32_t D,
                                        int32_t n_slices, const void *const *A, const void *const *B,
                                        const int64_t *out_sizes, const int64_t *out_offsets, int32_t S,
-                                       int32_t r_max, const int32_t *ranks, const float *scale,
-                                       const void *seg, const int32_t *idx, int32_t active_hint, float *v,
-                                       void *y, int64_t ldy, int32_t *errors_host, hipStream_t stream);
+                                       int32_t r_max, const int32_t *ranks, int32_t b_layout,
+                                       const float *scale, const void *seg, const int32_t *idx,
+                                       int32_t active_hint, float *v, void *y, int64_t ldy,
+                                       int32_t *errors_host, hipStream_t stream);
+
+/*
+ * Mask ("laning") form of lora_shrink_expand, for batches whose adapters
+ * stacked have few rank lanes: S * r_max <= 128.  "[Hardware][TPU][V1] Better
+ * tpu multilora compilation" reports a masked formulation beating the
+ * per-token gather on TPU, and LoRA laning (adapters packed side by side so
+ * that one matrix product serves them all) cutting the number of products.
+ * Here every 16-token tile of x is multiplied with all L = S * r_max stacked
+ * rows of A_i (the tensor [S][r_max][D] read as one [L][D] matrix), each
+ * token keeps the lanes of its own slot (times its scale, columns k < r_s),
+ * and the expand multiplies all lanes of B with v masked to the token's own
+ * lanes.  The result is that of lora_shrink_expand; no segment record is
+ * needed (idx is read directly), and every row of x is read whatever its
+ * slot (a dense product), while rows of y of tokens without a valid slot (or
+ * whose slot has rank 0) are never written.
+ *   arguments    as lora_shrink_expand, minus seg, with B in the padded layout
+ *   idx          [T] int32 device slots (-1 base-only; out-of-range = base-only)
+ *   v            nullable; when given, written in full as lora_shrink writes it
+ *   workspace    device, 256-byte aligned, >= lora_mask_workspace_bytes(dt, T,
+ *                D, S, n_slices, r_max) bytes: the shrink's fp32 partial sums
+ *                (no clearing needed; contents are overwritten)
+ * Two launches (the dense shrink in K parts, the masked expand summing the
+ * parts in order).  LORA_ERR_UNSUPPORTED when S * r_max > 128; other errors
+ * and the no-op gate as lora_shrink_expand.
+ */
+size_t lora_mask_workspace_bytes(lora_dtype dt, int32_t T, int32_t D, int32_t S, int32_t n_slices,
+                                 int32_t r_max);
+
+lora_status lora_shrink_expand_mask(lora_dtype dt, const void *x, int64_t ldx, int32_t T, int32_t D,
+                                    int32_t n_slices, const void *const *A, const void *const *B,
+                                    const int64_t *out_sizes, const int64_t *out_offsets, int32_t S,
+                                    int32_t r_max, const int32_t *ranks, const float *scale,
+                                    const int32_t *idx, int32_t active_hint, float *v, void *y,
+                                    int64_t ldy, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /*
  * Copy the count of waits that gave up (int32 word 0 of a lora_shrink_expand

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = glsa.lib()
-    assert lib.lora_abi_version() == 1
+    assert lib.lora_abi_version() == 2
     for code, name in [(0, b"LORA_OK"), (1, b"LORA_ERR_INVALID_ARG"), (2, b"LORA_ERR_UNSUPPORTED"),
                        (3, b"LORA_ERR_INDEX"), (4, b"LORA_ERR_HIP")]:
         assert lib.lora_status_string(code) == name
@@ -78,14 +78,14 @@ def _shrink(**kw):
 
 def _expand(**kw):
     a = dict(dt=2, v=FAKE, vss=0, T=8, n_slices=1, B=[FAKE], sizes=[64], offs=[0], S=4,
-             r_max=16, ranks=None, seg=FAKE, active=1, y=FAKE, ldy=64)
+             r_max=16, ranks=None, b_layout=0, seg=FAKE, active=1, y=FAKE, ldy=64)
     a.update(kw)
     n = max(1, len(a["B"]))
     B = (ctypes.c_void_p * n)(*a["B"])
     sizes = (ctypes.c_int64 * n)(*a["sizes"])
     offs = (ctypes.c_int64 * n)(*a["offs"])
     return glsa.lib().lora_expand(a["dt"], a["v"], a["vss"], a["T"], a["n_slices"], B, sizes,
-                                  offs, a["S"], a["r_max"], a["ranks"], a["seg"], a["active"],
+                                  offs, a["S"], a["r_max"], a["ranks"], a["b_layout"], a["seg"], a["active"],
                                   a["y"], a["ldy"], None)
 
 
@@ -126,6 +126,8 @@ def test_shrink_rejects_bad_arguments(kw, status):
     (dict(n_slices=2, B=[FAKE, FAKE], sizes=[32, 32], offs=[0, 16]), glsa.LORA_ERR_INVALID_ARG),
     (dict(ldy=0), glsa.LORA_ERR_UNSUPPORTED),
     (dict(B=[FAKE + 4]), glsa.LORA_ERR_UNSUPPORTED),
+    (dict(b_layout=2), glsa.LORA_ERR_INVALID_ARG),
+    (dict(b_layout=-1), glsa.LORA_ERR_INVALID_ARG),
 ])
 def test_expand_rejects_bad_arguments(kw, status):
     assert _expand(**kw) == status
@@ -173,8 +175,8 @@ def test_python_binding_raises_lora_error():
 
 def _fused(**kw):
     a = dict(dt=1, x=FAKE, ldx=64, T=8, D=64, n_slices=1, A=[FAKE], B=[FAKE], sizes=[64],
-             offs=[0], S=4, r_max=16, ranks=None, scale=None, seg=FAKE, idx=None, active=1, v=None,
-             y=FAKE, ldy=64, ws=FAKE, ws_bytes=None)
+             offs=[0], S=4, r_max=16, ranks=None, b_layout=0, scale=None, seg=FAKE, idx=None, active=1,
+             v=None, y=FAKE, ldy=64, ws=FAKE, ws_bytes=None)
     a.update(kw)
     n = a["n_slices"]
     if a["ws_bytes"] is None:
@@ -184,8 +186,8 @@ def _fused(**kw):
     sizes = (ctypes.c_int64 * len(a["sizes"]))(*a["sizes"])
     offs = (ctypes.c_int64 * len(a["offs"]))(*a["offs"])
     return glsa.lib().lora_shrink_expand(a["dt"], a["x"], a["ldx"], a["T"], a["D"], n, A, B, sizes,
-                                         offs, a["S"], a["r_max"], a["ranks"], a["scale"], a["seg"],
-                                         a["idx"], a["active"], a["v"], a["y"], a["ldy"], a["ws"],
+                                         offs, a["S"], a["r_max"], a["ranks"], a["b_layout"], a["scale"],
+                                         a["seg"], a["idx"], a["active"], a["v"], a["y"], a["ldy"], a["ws"],
                                          a["ws_bytes"], None)
 
 
@@ -212,6 +214,7 @@ def test_fused_workspace_bytes():
     (dict(v=FAKE + 8), glsa.LORA_ERR_UNSUPPORTED),      # misaligned v
     (dict(A=[0]), glsa.LORA_ERR_INVALID_ARG),
     (dict(B=[0]), glsa.LORA_ERR_INVALID_ARG),
+    (dict(b_layout=5), glsa.LORA_ERR_INVALID_ARG),
 ])
 def test_fused_rejects_bad_arguments(kw, status):
     assert _fused(**kw) == status
@@ -342,8 +345,8 @@ def test_binding_rejects_host_tensors_for_device_arguments(monkeypatch):
 
 def _noalloc(**kw):
     a = dict(dt=2, x=FAKE, ldx=64, T=8, D=64, n_slices=1, A=[FAKE], B=[FAKE], sizes=[64],
-             offs=[0], S=4, r_max=16, ranks=None, scale=None, seg=FAKE, idx=None, active=1, v=None,
-             y=FAKE, ldy=64, err=None)
+             offs=[0], S=4, r_max=16, ranks=None, b_layout=0, scale=None, seg=FAKE, idx=None, active=1,
+             v=None, y=FAKE, ldy=64, err=None)
     a.update(kw)
     n = a["n_slices"]
     A = (ctypes.c_void_p * len(a["A"]))(*a["A"])
@@ -352,7 +355,7 @@ def _noalloc(**kw):
     offs = (ctypes.c_int64 * len(a["offs"]))(*a["offs"])
     return glsa.lib().lora_shrink_expand_noalloc(
         a["dt"], a["x"], a["ldx"], a["T"], a["D"], n, A, B, sizes, offs, a["S"], a["r_max"], a["ranks"],
-        a["scale"], a["seg"], a["idx"], a["active"], a["v"], a["y"], a["ldy"], a["err"], None)
+        a["b_layout"], a["scale"], a["seg"], a["idx"], a["active"], a["v"], a["y"], a["ldy"], a["err"], None)
 
 
 def test_noalloc_scratch_limit_matches_header():
