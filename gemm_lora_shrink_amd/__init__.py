@@ -28,7 +28,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblora_mi355x.so")
+# LORA_MI355X_LIB names another build of this same library (the host-checks
+# test loads one built with the address and undefined-behaviour sanitizers).
+LIB_PATH = os.environ.get("LORA_MI355X_LIB") or os.path.join(_HERE, "liblora_mi355x.so")
 
 LORA_OK = 0
 LORA_ERR_INVALID_ARG = 1

@@ -54,7 +54,17 @@ extern "C" {
 /* Most adapter slots one batch may index. */
 #define LORA_MAX_SLOTS 1024
 
-typedef enum {
+/* The enums below are 32-bit integers on the ABI.  A caller may pass any
+ * int32 value in an enum argument (the library rejects those it does not
+ * know); under C++ the enums get int32_t as their underlying type so that
+ * such a value is well defined there too. */
+#ifdef __cplusplus
+#define LORA_ENUM enum : int32_t
+#else
+#define LORA_ENUM enum
+#endif
+
+typedef LORA_ENUM {
   LORA_OK = 0,
   LORA_ERR_INVALID_ARG = 1, /* a null pointer, a negative size, a bad stride */
   LORA_ERR_UNSUPPORTED = 2, /* a valid request outside the documented limits */
@@ -62,7 +72,7 @@ typedef enum {
   LORA_ERR_HIP = 4          /* the HIP runtime refused a launch or copy */
 } lora_status;
 
-typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
+typedef LORA_ENUM { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
 
 /* How lora_build_segments splits each slot's tokens into kernel work items.
  *   AUTO: slots with at least lora_sgmv_min_tokens() tokens go to the segmented
@@ -74,7 +84,7 @@ typedef enum { LORA_F32 = 0, LORA_F16 = 1, LORA_BF16 = 2 } lora_dtype;
  *   BGMV: every slot in groups of at most 16 tokens.
  *   SGMV: every slot in tiles of at most 64 tokens.
  * fp32 data always runs on the gather kernels, whatever the mode. */
-typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode;
+typedef LORA_ENUM { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora_mode;
 
 /* How the rows of one slot's B are stored inside the slot's [out_i][r_max]
  * region of a stacked B_i [S][out_i][r_max] ("Add multi-LoRA support",
@@ -88,7 +98,7 @@ typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_BGMV = 1, LORA_MODE_SGMV = 2 } lora
  *              packed rows is never read.  Entries between r_s and the rounded
  *              stride are ignored.  lora_copy_padded places an adapter this way
  *              when given that stride as dst_ld (see lora_copy_padded). */
-typedef enum { LORA_B_PADDED = 0, LORA_B_RANK_ROWS = 1 } lora_b_layout;
+typedef LORA_ENUM { LORA_B_PADDED = 0, LORA_B_RANK_ROWS = 1 } lora_b_layout;
 
 /* ------------------------------------------------------------------------ */
 /* Segment record                                                           */
@@ -128,7 +138,7 @@ typedef enum { LORA_B_PADDED = 0, LORA_B_RANK_ROWS = 1 } lora_b_layout;
  * Entries past the counts are unspecified.  The record is bit-exact and
  * deterministic for a given (idx, S, mode).
  */
-typedef enum {
+typedef LORA_ENUM {
   LORA_SEG_INFO = 0,
   LORA_SEG_PERM = 1,
   LORA_SEG_SLOT = 2,
