@@ -166,7 +166,10 @@ int32_t lora_sgmv_min_tokens(void);
  *   info_host  [host] nullable; pinned host memory of 16 int32.  When given, the
  *              16 info words are copied there asynchronously on `stream`; they
  *              are valid after the stream is synchronised.
- * One single-workgroup kernel; nothing else runs.
+ * One kernel; nothing else runs.  Below 512 tokens it is one workgroup;
+ * from 512 tokens on (LORA_SEG_WIDE_MIN_T in the environment overrides the
+ * threshold) one workgroup per 1024 tokens, which never wait for one another.
+ * The record is the same either way.
  */
 lora_status lora_build_segments(const int32_t *idx, int32_t T, int32_t S, int32_t mode,
                                 void *seg, int32_t *info_host, hipStream_t stream);
