@@ -714,6 +714,7 @@ def main():
         err_y=head.get("err_y"), err_v=head.get("err_v"), meta_bitexact=head.get("meta_bitexact"),
         workspace_errors=head.get("workspace_errors"),
         calls=head.get("calls"),
+        noop=head.get("noop"),
         roofline=roofline,
         cpu_baseline=cpu,
         configs=configs,
