@@ -30,6 +30,8 @@ constexpr int kThreads = 256;
 // unit.
 constexpr int kSubs = kTile / 16;                              // 16-token sub-blocks per item
 constexpr int kVRow = LORA_MAX_RANK + 8;                       // padded 16-bit LDS row of v
+constexpr int kTileRun = 2;              // column tiles per unit of a segmented tile (see the kernel)
+constexpr int kGroupRun = 4 * kTileRun;  // ... of a gather group
 
 // One tile unit: the column tiles [ct_begin, ct_end) of an item of up to 64
 // tokens (NSUB 16-token sub-blocks; sub-blocks past the item's tokens hold no
@@ -37,8 +39,9 @@ constexpr int kVRow = LORA_MAX_RANK + 8;                       // padded 16-bit 
 // thread's v row (row tid / 4, -1 past the item's count).  The v rows, the
 // first column tile's y and its B rows are all requested before any of them
 // is waited for; the fp32 v rows are then converted into the 16-bit hi/lo
-// operands in LDS.
-template <typename Elem, int NSUB>
+// operands in LDS.  A unit has at most RUN column tiles (a compile-time bound,
+// so that no load is issued for a tile past the last one a unit can have).
+template <typename Elem, int NSUB, int RUN>
 __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, int* s_tok, float* s_unscale,
                                    Elem (*s_vhi)[kVRow], Elem (*s_vlo)[kVRow], float (*s_tr)[16][kTrRow],
                                    int slice, int s, int r, int out, int ct_begin, int ct_end) {
@@ -214,13 +217,20 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
   // two tiles per iteration, so that the register buffers alternate without
   // copies; the next tile's y and B rows are in flight during each tile
   u32x4 ynext[NSUB][2], bnext[4][2];
-  for (int ct = ct_begin; ct < ct_end; ct += 2) {
-    load_y(ct + 1, ynext);
-    load_b(ct + 1, bnext);
+#pragma unroll
+  for (int i = 0; i < RUN; i += 2) {
+    const int ct = ct_begin + i;
+    if (ct >= ct_end) break;
+    if (i + 1 < RUN) {
+      load_y(ct + 1, ynext);
+      load_b(ct + 1, bnext);
+    }
     compute_tile(ct, yold, bop);
-    if (ct + 1 >= ct_end) break;
-    load_y(ct + 2, yold);
-    load_b(ct + 2, bop);
+    if (i + 1 >= RUN || ct + 1 >= ct_end) break;
+    if (i + 2 < RUN) {
+      load_y(ct + 2, yold);
+      load_b(ct + 2, bop);
+    }
     compute_tile(ct + 1, ynext, bnext);
   }
 }
@@ -266,28 +276,28 @@ __device__ inline void expand_unit(const ExpandParams& p, int slice, bool tiles,
                               ct_end);
     return;
   }
-  expand_tile<Elem, kSubs>(p, tok(tid >> 2, tw_v), (it.cnt + 15) >> 4, s_tok, s_unscale, s_vhi, s_vlo, s_tr,
+  expand_tile<Elem, kSubs, kTileRun>(p, tok(tid >> 2, tw_v), (it.cnt + 15) >> 4, s_tok, s_unscale, s_vhi, s_vlo, s_tr,
                            slice, s, r, out, ct_begin, ct_end);
   lds_barrier();  // the next unit rewrites s_tok and the v operands
 }
 
-// The work is the pairs (item, 256-column tile) of every slice.  Each slice's
-// column tiles are cut into blocks of C, and the pairs are ordered by slice,
-// block, item (gather groups first), column tile.  A tile pair weighs
-// kTileWeight and a group pair 1 (a tile holds up to four times the tokens).
-// Share k of G takes the pairs whose weighted start lies in
-// [W k / G, W (k + 1) / G): a contiguous run, so that the per-item set-up
-// (tokens, v operands) is paid about once or twice per workgroup.  The shares
-// of one XCD's workgroups are adjacent.
-//   C is a whole slice (item order) unless the B rows of the slots one XCD
-// sees would not stay in its L2; then C is about the pairs per share, so that
-// the items of one slot, which read the same B rows, are in adjacent shares
-// and are taken at the same time by workgroups of one XCD.
-//   G is the grid, or the number of pairs when that is smaller (rounded up to
-// a multiple of kXcds): shares then go to the first workgroups of every XCD,
-// which the hardware places on distinct compute units.
-constexpr int kTileWeight = 4;
-constexpr int64_t kL2Bytes = 4 << 20;  // per XCD
+// The work is cut into units (item, slice, run of column tiles): a run of
+// kTileRun 256-column tiles for a segmented tile (64 tokens), of kGroupRun for
+// a gather group (16 tokens), so that every unit updates about the same bytes
+// of y.  Units are ordered by slice, item (gather groups first), run, and
+// taken window by window: round j of the kernel covers units [j G, (j + 1) G),
+// unit j G + q going to the workgroup with position q.  All workgroups thus
+// update y inside one compact window of rows at any time, which the HBM
+// serves faster than the same read-modify-write traffic spread over the whole
+// of y (a workgroup per contiguous share: 54 -> 50.5 us for the fused-QKV
+// prefill at 8192 tokens).  Positions are XCD-major (the workgroups of XCD x,
+// blockIdx % 8 == x, hold positions x G / 8 .. (x + 1) G / 8 - 1), so the
+// consecutive units of one item -- which read the same v rows, and items of
+// one slot the same B rows -- run on one XCD and share its L2.  Runs of two
+// tiles keep the per-unit set-up (tokens, v operands) to one per 128 KB of y
+// traffic; runs of one tile pay it twice as often, runs of four leave the last
+// round short.  With fewer units than workgroups, G is the units rounded up
+// to a multiple of kXcds.
 
 template <typename Elem>
 __global__ __launch_bounds__(kThreads, 2) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles) {
@@ -299,74 +309,40 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_expand_kernel(ExpandParams p
 
   const int64_t n_g = use_groups ? record_items(p.rec, p.T, p.S, false) : 0;
   const int64_t n_t = use_tiles ? record_items(p.rec, p.T, p.S, true) : 0;
-  const int64_t per_col = n_g + kTileWeight * n_t;  // weight of one column tile of every item
   auto n_cols = [&](int i) { return (int)ceil_div(p.out_size[i], kExpandColsPerWG); };
-  int64_t W = 0, pairs = 0, max_out = 0;
-  int max_cols = 1;
-  for (int i = 0; i < p.n_slices; ++i) {
-    W += n_cols(i) * per_col;
-    pairs += n_cols(i) * (n_g + n_t);
-    max_cols = max(max_cols, n_cols(i));
-    max_out = max(max_out, p.out_size[i]);
-  }
-  // grid and pair counts are multiples of kXcds once rounded
-  const int64_t G = min((int64_t)gridDim.x, max((int64_t)kXcds, ceil_div(pairs, kXcds) * kXcds));
+  int64_t units = 0;
+  for (int i = 0; i < p.n_slices; ++i)
+    units += n_g * ceil_div(n_cols(i), kGroupRun) + n_t * ceil_div(n_cols(i), kTileRun);
+  // with fewer units than workgroups, the first workgroups of every XCD take
+  // them (the hardware places those on distinct compute units)
+  const int64_t G = min((int64_t)gridDim.x, max((int64_t)kXcds, ceil_div(units, kXcds) * kXcds));
   const int64_t lb = blockIdx.x / kXcds;
-  if (lb >= G / kXcds) return;  // uniform: this workgroup has no share
-  const int64_t k = (blockIdx.x % kXcds) * (G / kXcds) + lb;
-  const int64_t w0 = W * k / G, w1 = W * (k + 1) / G;
-  const int64_t n_seg = max(1, p.rec[kNumSegments]);  // distinct slots in the batch
-  const bool blocks = ceil_div(n_seg, kXcds) * max_out * p.r_max * (int64_t)sizeof(Elem) > kL2Bytes;
-  const int C = blocks ? (int)min((int64_t)max_cols, max((int64_t)1, ceil_div(pairs, G))) : max_cols;
-
-  // blocks in order: (slice, first column tile c0, width cb); base is the
-  // block's weighted start
-  int slice = 0, c0 = 0;
-  int64_t base = 0;
-  auto width = [&]() { return min(C, n_cols(slice) - c0); };
-  auto next_block = [&]() {
-    base += width() * per_col;
-    c0 += C;
-    if (c0 >= n_cols(slice)) {
-      c0 = 0;
+  if (lb >= G / kXcds) return;  // uniform: no unit for this workgroup
+  const int64_t q = (blockIdx.x % kXcds) * (G / kXcds) + lb;
+  // walk this workgroup's units u = q, q + G, ...: (slice, item, run) from u,
+  // with the slice's unit counts peeled off as u grows
+  int slice = 0;
+  int64_t first = 0;  // first unit of `slice`
+  for (int64_t u = q;; u += G) {
+    int gu = 0, tu = 0;
+    int64_t nu = 0;
+    while (slice < p.n_slices) {
+      gu = (int)ceil_div(n_cols(slice), kGroupRun);  // units per gather group
+      tu = (int)ceil_div(n_cols(slice), kTileRun);   // units per segmented tile
+      nu = n_g * gu + n_t * tu;
+      if (u < first + nu) break;
+      first += nu;
       ++slice;
     }
-  };
-  // the first pair whose weighted start is >= w0
-  while (slice < p.n_slices && base + width() * per_col <= w0) next_block();
-  int64_t item = 0;
-  int ct = 0;  // column tile within the block
-  if (slice < p.n_slices) {
-    const int cb = width();
-    const int64_t rel = w0 - base;
-    if (rel < n_g * cb) {
-      item = rel / cb;
-      ct = (int)(rel % cb);
-    } else {
-      const int64_t q = ceil_div(rel - n_g * cb, kTileWeight);
-      item = n_g + q / cb;
-      ct = (int)(q % cb);
-    }
-  }
-  while (slice < p.n_slices) {
-    const int cb = width();
-    if (item >= n_g + n_t) {  // past the block's last item
-      next_block();
-      item = 0;
-      ct = 0;
-      continue;
-    }
-    const bool tiles = item >= n_g;
-    const int64_t pos = base + (tiles ? n_g * cb + kTileWeight * ((item - n_g) * cb + ct) : item * cb + ct);
-    if (pos >= w1) break;
-    // the item's column tiles of this block from ct whose pairs start before w1
-    const int64_t room = tiles ? ceil_div(w1 - pos, kTileWeight) : w1 - pos;
-    const int ct_end = (int)(cb - ct < room ? cb : ct + room);
-    expand_unit<Elem>(p, slice, tiles, tiles ? item - n_g : item, c0 + ct, c0 + ct_end, s_tok, s_unscale, s_vhi,
-                      s_vlo, s_tr);
-    if (ct_end < cb) break;  // the share ends inside this item
-    ++item;
-    ct = 0;
+    if (slice >= p.n_slices) break;
+    const int64_t rel = u - first;
+    const bool tiles = rel >= n_g * gu;
+    const int64_t rr = tiles ? rel - n_g * gu : rel;
+    const int per = tiles ? tu : gu, run = tiles ? kTileRun : kGroupRun;
+    const int64_t item = rr / per;
+    const int ct0 = (int)(rr % per) * run;
+    const int ct1 = min(n_cols(slice), ct0 + run);
+    expand_unit<Elem>(p, slice, tiles, item, ct0, ct1, s_tok, s_unscale, s_vhi, s_vlo, s_tr);
   }
 }
 
