@@ -235,26 +235,44 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
   }
 }
 
+// The words of an item a unit needs: its header and the token words of this
+// thread (the token of its v row -- tile path: row tid / 4 -- and those of its
+// MFMA column and y rows -- gather path).  The kernel requests them one unit
+// ahead, so that they are in registers when the unit starts.
+struct UnitWords {
+  u32x4 head;
+  int tw_v, tw_n, tw_y0, tw_y1;
+};
+__device__ inline UnitWords load_unit_words(const ExpandParams& p, bool tiles, int64_t li) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int32_t* ip = item_ptr(p.rec, p.T, p.S, tiles, li);
+  UnitWords w;
+  w.head = *reinterpret_cast<const u32x4*>(ip);  // items are 16-byte aligned
+  w.tw_v = ip[4 + (tiles ? (tid >> 2) : ((tid >> 2) & (kGroup - 1)))];
+  w.tw_n = ip[4 + (lane & 15)];
+  w.tw_y0 = ip[4 + (lane >> 3)];
+  w.tw_y1 = ip[4 + (lane >> 3) + 8];
+  return w;
+}
+
 // One unit: the column tiles [ct_begin, ct_end) of item `li` of a list
-// (tiles or gather groups) for one slice.
+// (tiles or gather groups) for one slice, from its words w; s_rank holds
+// every slot's rank.
 template <typename Elem>
-__device__ inline void expand_unit(const ExpandParams& p, int slice, bool tiles, int64_t li, int ct_begin,
-                                   int ct_end, int* s_tok, float* s_unscale, Elem (*s_vhi)[kVRow],
-                                   Elem (*s_vlo)[kVRow], float (*s_tr)[16][kTrRow]) {
+__device__ inline void expand_unit(const ExpandParams& p, int slice, bool tiles, const UnitWords& w, int ct_begin,
+                                   int ct_end, const int* s_rank, int* s_tok, float* s_unscale,
+                                   Elem (*s_vhi)[kVRow], Elem (*s_vlo)[kVRow], float (*s_tr)[16][kTrRow]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int n = lane & 15, yr = lane >> 3;
   const int out = (int)p.out_size[slice];
-  // The item's header and the token words this thread needs arrive in one
-  // memory round trip: the token of its v row (tile path: row tid / 4) and
-  // those of its MFMA column and y rows (gather path).
-  const int32_t* ip = item_ptr(p.rec, p.T, p.S, tiles, li);
-  const int tw_v = ip[4 + (tiles ? (tid >> 2) : ((tid >> 2) & (kGroup - 1)))];
-  const int tw_n = ip[4 + n], tw_y0 = ip[4 + yr], tw_y1 = ip[4 + yr + 8];
-  Item it;
-  if (!read_item(p.rec, p.T, p.S, tiles, li, it)) return;
-  const int s = it.slot;
-  const int r = slot_rank(p.ranks, s, p.r_max);
+  const int tw_v = w.tw_v, tw_n = w.tw_n, tw_y0 = w.tw_y0, tw_y1 = w.tw_y1;
+  const Item it{(int)w.head[0], (int)w.head[1], (int)w.head[2], (int)w.head[3]};
+  const int cap = tiles ? kTile : kGroup;
+  if (!(it.slot >= 0 && it.slot < p.S && it.p0 >= 0 && it.cnt > 0 && it.cnt <= cap && it.p0 + it.cnt <= p.T))
+    return;
+  const int s = __builtin_amdgcn_readfirstlane(it.slot);
+  const int r = __builtin_amdgcn_readfirstlane(s_rank[s]);
   if (r == 0) return;
   // token k of the item, clamped into [0, T); -1 past its count
   auto tok = [&](int k, int t) { return k < it.cnt ? (t < 0 ? 0 : (t >= p.T ? p.T - 1 : t)) : -1; };
@@ -303,6 +321,7 @@ template <typename Elem>
 __global__ __launch_bounds__(kThreads, 2) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles) {
   __shared__ int s_tok[kTile];
   __shared__ float s_unscale[kTile];
+  __shared__ int s_rank[LORA_MAX_SLOTS];
   __shared__ __attribute__((aligned(16))) Elem s_vhi[kTile][kVRow];
   __shared__ __attribute__((aligned(16))) Elem s_vlo[kTile][kVRow];
   __shared__ __attribute__((aligned(16))) float s_tr[4][16][kTrRow];
@@ -319,30 +338,48 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_expand_kernel(ExpandParams p
   const int64_t lb = blockIdx.x / kXcds;
   if (lb >= G / kXcds) return;  // uniform: no unit for this workgroup
   const int64_t q = (blockIdx.x % kXcds) * (G / kXcds) + lb;
-  // walk this workgroup's units u = q, q + G, ...: (slice, item, run) from u,
-  // with the slice's unit counts peeled off as u grows
-  int slice = 0;
-  int64_t first = 0;  // first unit of `slice`
-  for (int64_t u = q;; u += G) {
-    int gu = 0, tu = 0;
-    int64_t nu = 0;
-    while (slice < p.n_slices) {
-      gu = (int)ceil_div(n_cols(slice), kGroupRun);  // units per gather group
-      tu = (int)ceil_div(n_cols(slice), kTileRun);   // units per segmented tile
-      nu = n_g * gu + n_t * tu;
-      if (u < first + nu) break;
-      first += nu;
-      ++slice;
+  // every slot's rank, in LDS: a unit's rank costs no memory round trip
+  for (int i = threadIdx.x; i < p.S; i += kThreads) s_rank[i] = slot_rank(p.ranks, i, p.r_max);
+  // unit u: its slice, list, item and column tiles
+  struct Unit {
+    bool ok, tiles;
+    int slice, ct0, ct1;
+    int64_t item;
+  };
+  auto decode = [&](int64_t u) {
+    Unit d{false, false, 0, 0, 0, 0};
+    for (int i = 0; i < p.n_slices; ++i) {
+      const int gu = (int)ceil_div(n_cols(i), kGroupRun);  // units per gather group
+      const int tu = (int)ceil_div(n_cols(i), kTileRun);   // units per segmented tile
+      const int64_t nu = n_g * gu + n_t * tu;
+      if (u < nu) {
+        d.ok = true;
+        d.slice = i;
+        d.tiles = u >= n_g * gu;
+        const int64_t rr = d.tiles ? u - n_g * gu : u;
+        const int per = d.tiles ? tu : gu, run = d.tiles ? kTileRun : kGroupRun;
+        d.item = rr / per;
+        d.ct0 = (int)(rr % per) * run;
+        d.ct1 = min(n_cols(i), d.ct0 + run);
+        return d;
+      }
+      u -= nu;
     }
-    if (slice >= p.n_slices) break;
-    const int64_t rel = u - first;
-    const bool tiles = rel >= n_g * gu;
-    const int64_t rr = tiles ? rel - n_g * gu : rel;
-    const int per = tiles ? tu : gu, run = tiles ? kTileRun : kGroupRun;
-    const int64_t item = rr / per;
-    const int ct0 = (int)(rr % per) * run;
-    const int ct1 = min(n_cols(slice), ct0 + run);
-    expand_unit<Elem>(p, slice, tiles, item, ct0, ct1, s_tok, s_unscale, s_vhi, s_vlo, s_tr);
+    return d;
+  };
+  lds_barrier();
+  // this workgroup's units u = q, q + G, ..., each unit's words requested
+  // while the unit before it runs
+  Unit cur = decode(q);
+  UnitWords cw{};
+  if (cur.ok) cw = load_unit_words(p, cur.tiles, cur.item);
+  for (int64_t u = q; cur.ok; u += G) {
+    const Unit nxt = decode(u + G);
+    UnitWords nw{};
+    if (nxt.ok) nw = load_unit_words(p, nxt.tiles, nxt.item);
+    expand_unit<Elem>(p, cur.slice, cur.tiles, cw, cur.ct0, cur.ct1, s_rank, s_tok, s_unscale, s_vhi, s_vlo, s_tr);
+    cur = nxt;
+    cw = nw;
   }
 }
 
