@@ -57,6 +57,7 @@ namespace {
 constexpr int kFThreads = kUnitThreads;
 constexpr int kFRing = 16384;        // per-wave LDS ring: 64 KB per workgroup, two workgroups per CU
 constexpr int kMaxParts = 4;         // K parts per chunk
+constexpr int kSumBatch = 4;         // parts whose slabs a consumer loads at once
 constexpr int kFusedUnits = 1024;    // at most this many producer slabs when chunks are cut into K parts
 constexpr int kSpinLimit = 1 << 20;  // polls (about a microsecond each) before a wait gives up
 constexpr int kZeroRowsF = 64;       // tail entries per zero unit
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   __shared__ int s_tok[16];
   __shared__ IdxTables s_it;
 
+  warm_args(f);
   const ShrinkParams& p = f.sp;
   const int32_t* rec = p.rec;
   const int T = p.T, S = p.S, r_max = p.r_max, ns = p.n_slices;
@@ -477,20 +479,22 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
         const bool ok = tok_n >= 0 && ks < nks && k0 < r;
         f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
         if (ks < nks) {  // uniform
-          // every part's loads in flight at once, then the sum in part order
-          // (parts past kp read zeros)
-          f32x4 w[kMaxParts][2];
+          // the parts' loads in flight kSumBatch at a time, summed in part
+          // order (parts past kp read zeros)
+          for (int q0 = 0; q0 < kp; q0 += kSumBatch) {
+            f32x4 w[kSumBatch][2];
 #pragma unroll
-          for (int q = 0; q < kMaxParts; ++q) {
-            const bool okq = ok && q < kp;
-            const float* src = slabs + (okq ? q * slab_floats + k0 : 0);
-            w[q][0] = ldf4_or0(src, okq);
-            w[q][1] = ldf4_or0(src + 4, okq);
-          }
+            for (int j = 0; j < kSumBatch; ++j) {
+              const bool okq = ok && q0 + j < kp;
+              const float* src = slabs + (okq ? (q0 + j) * slab_floats + k0 : 0);
+              w[j][0] = ldf4_or0(src, okq);
+              w[j][1] = ldf4_or0(src + 4, okq);
+            }
 #pragma unroll
-          for (int q = 0; q < kMaxParts; ++q) {
-            a0 += w[q][0];
-            a1 += w[q][1];
+            for (int j = 0; j < kSumBatch; ++j) {
+              a0 += w[j][0];
+              a1 += w[j][1];
+            }
           }
         }
 #pragma unroll
