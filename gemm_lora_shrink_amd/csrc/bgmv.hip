@@ -60,6 +60,7 @@ __device__ inline void store_y4(Elem* dst, const float* acc, typename YChunk<Ele
 
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(ExpandParams p, int use_tiles, int n_ct) {
+  warm_args(p);
   using Tr = Traits<Elem>;
   __shared__ __attribute__((aligned(16))) float s_v[kGroup][LORA_MAX_RANK];
   __shared__ int s_tok[kGroup];

@@ -28,6 +28,7 @@ struct EmbParams {
 
 template <typename Elem>
 __global__ __launch_bounds__(256) void embedding_shrink_kernel(EmbParams p) {
+  warm_args(p);
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t t = g >> 4;
   const int k0 = (int)(g & 15) * 4;

@@ -67,6 +67,7 @@ __device__ inline bool row_gets_delta(const MaskParams& p, int t) {
 // blocks w and w + 4 (16 lanes each) over the part's K steps.
 template <typename Elem>
 __global__ __launch_bounds__(kMaskThreads) void mask_shrink_kernel(MaskParams p) {
+  warm_args(p);
   using M = StepMma<Elem>;
   constexpr int kVec = Traits<Elem>::kVec;
   constexpr int kStep = 4 * kVec;
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(kMaskThreads) void mask_shrink_kernel(MaskParams p)
 // columns 64 w .. 64 w + 63 of the tile, as the gather path's group unit does.
 template <typename Elem>
 __global__ __launch_bounds__(kMaskThreads, 2) void mask_expand_kernel(MaskParams p) {
+  warm_args(p);
   constexpr int kVec = Traits<Elem>::kVec;
   constexpr int kStep = 4 * kVec;
   constexpr int kMaxQ = kMaskMaxLanes / kStep;  // K steps over the lanes

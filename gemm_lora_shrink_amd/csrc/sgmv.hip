@@ -319,6 +319,7 @@ __device__ inline void expand_unit(const ExpandParams& p, int slice, bool tiles,
 
 template <typename Elem>
 __global__ __launch_bounds__(kThreads, 2) void mfma_expand_kernel(ExpandParams p, int use_groups, int use_tiles) {
+  warm_args(p);
   __shared__ int s_tok[kTile];
   __shared__ float s_unscale[kTile];
   __shared__ int s_rank[LORA_MAX_SLOTS];

@@ -58,6 +58,7 @@ struct Split {
 template <typename Elem>
 __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int use_tiles, int use_groups,
                                                             int resident, int cleared) {
+  warm_args(p);
   __shared__ __attribute__((aligned(1024))) char s_lds[kWaves * kRingBytes];
   __shared__ int s_tok[kTile];
 
