@@ -534,7 +534,9 @@ def run_config(name, args, torch, glsa, dev, copy_gbs, headline):
     alg = [algorithmic(p) for p in problems]
     seg_b = segment_bytes(T, alg[0]["n_active"])
     calls = {}
-    calls["segments"] = dict(kernel="build_segments_kernel", us=call_time_us(do_segments), bytes=seg_b, flops=0,
+    # lora_build_segments runs its wide kernel from 512 tokens, the one-workgroup kernel below
+    seg_kernel = "build_segments_wide_kernel" if T >= 512 else "build_segments_kernel"
+    calls["segments"] = dict(kernel=seg_kernel, us=call_time_us(do_segments), bytes=seg_b, flops=0,
                              in_step=not build_in_call)
     for li, p in enumerate(problems):
         if fused and p.timed_expand and one_launch:
