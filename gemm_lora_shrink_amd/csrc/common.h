@@ -243,13 +243,17 @@ struct ExpandParams {
 // lines are first touched one after another puts one memory round trip per
 // line on the kernel's critical path (measured: about 1.2 us between the
 // grouping and the first producer unit of the one-launch kernel at decode
-// size).  warm_args requests every line of the block at kernel entry, all at
-// once.
+// size).  warm_args requests every line of the first kBytes of the kernel's
+// argument segment (the parameter block is every kernel's first argument) at
+// entry, all at once.  It reads through the segment pointer: taking the
+// address of the by-value parameter instead makes the compiler copy it to
+// scratch memory and read its fields from there.
 template <typename P>
-__device__ __forceinline__ void warm_args(const P& prm) {
+__device__ __forceinline__ void warm_args(const P&) {
   constexpr int kWords = (int)(sizeof(P) / 4);
   static_assert(kWords <= 8 * 16, "at most 8 lines");
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(&prm);
+  typedef const __attribute__((address_space(4))) uint32_t* KernargWords;  // the constant address space
+  const KernargWords w = (KernargWords)__builtin_amdgcn_kernarg_segment_ptr();
   auto line = [&](int i) { return w[16 * i < kWords ? 16 * i : kWords - 1]; };
   // one statement takes every line's word, so that the loads are issued
   // together and waited for once

@@ -99,25 +99,6 @@ struct IdxTables {
   int slot;
 };
 
-// Exclusive prefix sum of v over the workgroup's threads (thread order), and
-// the total.  Every thread calls it.
-__device__ inline int block_exscan(int v, int* scan, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int x = wave_inclusive_scan(v);  // DPP row shifts and broadcasts, no LDS round trips
-  if (lane == 63) scan[wave] = x;
-  lds_barrier();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int t = scan[w];
-    before += w < wave ? t : 0;
-    total += t;
-  }
-  lds_barrier();  // scan may be rewritten
-  return before + x - v;
-}
-
 // Chunk c of the record: gather group c, or for c >= n_g the 16-token quarter
 // (c - n_g) % 4 of tile (c - n_g) / 4.  The chunk's token words start at
 // `toks`; they can be loaded before the header is checked, so that header and
@@ -172,8 +153,12 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
   if constexpr (FROM_IDX) {
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i) {
+      // an unconditional load (a guarded one becomes a branch, and the
+      // compiler waits for every load in flight at the merge), masked after
       const int t = t_first + i;
-      const int k = i < tpt && t < T ? f.idx[t] : -1;
+      const bool in = i < tpt && t < T;
+      const int ld = f.idx[in ? t : 0];
+      const int k = in ? ld : -1;
       keys[i] = k >= 0 && k < S ? k : -1;
     }
     // the slots' ranks are requested with idx, so that a unit's rank costs no
@@ -195,7 +180,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       local += s < S ? (s_it.cnt[s] + 15) >> 4 : 0;
     }
     int total;
-    int ex = block_exscan(local, s_it.scan, total);
+    int ex = block_exscan<kWaves>(local, s_it.scan, total);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s = 4 * tid + j;
@@ -235,7 +220,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i) m += keys[i] == s ? 1 : 0;
     int tot;
-    int rk = block_exscan(m, s_it.scan, tot) - 16 * piece;  // rank of this thread's first match in the chunk
+    int rk = block_exscan<kWaves>(m, s_it.scan, tot) - 16 * piece;  // rank of this thread's first match in the chunk
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i)
       if (keys[i] == s) {

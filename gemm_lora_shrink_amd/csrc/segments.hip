@@ -89,13 +89,17 @@ __global__ __launch_bounds__(kWThreads) void build_segments_wide_kernel(const in
   // this wave's own chunk, then its chunks of the whole batch
   const int t_own = b * kWTokens + wave * 64 + lane;
   const bool own_valid = t_own < T;
-  const int own_raw = own_valid ? idx[t_own] : -1;
+  // unconditional loads: a guarded load becomes a branch, and the compiler
+  // waits for every load in flight at the merge; lanes past the batch read its
+  // last token and are masked afterwards
+  const int own_ld = idx[own_valid ? t_own : T - 1];
+  const int own_raw = own_valid ? own_ld : -1;
   int raw[kWBatch];
   auto load_batch = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < kWBatch; ++u) {
       const int t = (c0 + u * kWWaves) * 64 + lane;
-      raw[u] = t < T ? idx[t] : -1;
+      raw[u] = idx[t < T ? t : T - 1];
     }
   };
   load_batch(wave);
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(kWThreads) void build_segments_wide_kernel(const in
       const int c = c0 + u * kWWaves;
       if (c >= n_chunks) break;  // uniform
       const bool valid = c * 64 + lane < T;
-      const int k = key_of(raw[u]);
+      const int k = valid ? key_of(raw[u]) : S;
       if (valid && raw[u] != -1 && k == S) bad = 1;
       const bool before = c < own_first;  // uniform
       const uint64_t vmask = __ballot(valid);

@@ -136,6 +136,26 @@ __device__ inline void block_exclusive_scan4(int4& v, int4* wave_sums, int4& tot
   v = make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
 }
 
+// Exclusive prefix sum of one int over a workgroup of kW waves (thread order),
+// and the total.  Every thread calls it; scan holds kW ints of LDS.
+template <int kW>
+__device__ inline int block_exscan(int v, int* scan, int& total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int x = wave_inclusive_scan(v);  // DPP row shifts and broadcasts, no LDS round trips
+  if (lane == 63) scan[wave] = x;
+  lds_barrier();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const int t = scan[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  lds_barrier();  // scan may be rewritten
+  return before + x - v;
+}
+
 // Largest s in [0, n) with arr[s] <= key, for a non-decreasing arr with arr[0] <= key.
 __device__ inline int upper_slot(const int* arr, int n, int key) {
   int lo = 0, hi = n - 1;

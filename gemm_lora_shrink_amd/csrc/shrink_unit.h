@@ -64,7 +64,16 @@ constexpr int kBlockBytes = 2048;  // one batch of one 16-row block: 16 rows x 1
 // compiler, which cannot tell the ring's slots apart, would otherwise wait for
 // every load in flight before each LDS read.  M0 is saved and restored around
 // it.
+// The base and the LDS address are wave-uniform at every call; they go through
+// readfirstlane so that the compiler can prove it (free when it already can).
+__device__ inline const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
 __device__ inline void load_to_lds(const char* base, uint32_t voff, uint32_t lds) {
+  base = uniform_ptr(base);
+  lds = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -78,6 +87,8 @@ __device__ inline void load_to_lds(const char* base, uint32_t voff, uint32_t lds
 }
 // The same with a non-temporal hint, for rows read once.
 __device__ inline void load_to_lds_nt(const char* base, uint32_t voff, uint32_t lds) {
+  base = uniform_ptr(base);
+  lds = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -314,7 +325,7 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
 }
 
 template <typename Elem, int RB, bool XONCE, int RING>
-__device__ inline void contract_rb(const ShrinkParams& p, int nb, int cnt, int s, int r, int slice, int s0, int s1,
+__device__ __forceinline__ void contract_rb(const ShrinkParams& p, int nb, int cnt, int s, int r, int slice, int s0, int s1,
                                    bool partial, float* part, char* s_lds, const int* s_tok, int c_lo, int c_hi) {
   switch (nb) {
     case 1: contract_unit<Elem, RB, 1, XONCE, RING>(p, cnt, s, r, slice, s0, s1, partial, part, s_lds, s_tok, c_lo, c_hi); break;
@@ -325,7 +336,7 @@ __device__ inline void contract_rb(const ShrinkParams& p, int nb, int cnt, int s
 }
 
 template <typename Elem, bool XONCE, int RING>
-__device__ inline void contract_any(const ShrinkParams& p, int rbs, int nb, int cnt, int s, int r, int slice, int s0,
+__device__ __forceinline__ void contract_any(const ShrinkParams& p, int rbs, int nb, int cnt, int s, int r, int slice, int s0,
                                     int s1, bool partial, float* part, char* s_lds, const int* s_tok, int c_lo, int c_hi) {
   if (rbs == 1) contract_rb<Elem, 1, XONCE, RING>(p, nb, cnt, s, r, slice, s0, s1, partial, part, s_lds, s_tok, c_lo, c_hi);
   else if (rbs == 2) contract_rb<Elem, 2, XONCE, RING>(p, nb, cnt, s, r, slice, s0, s1, partial, part, s_lds, s_tok, c_lo, c_hi);

@@ -78,6 +78,16 @@ def _idx_cases():
                                                dtype="f16")
     yield "fp32_two_launches", random_problem(rng, T=200, D=64, out_sizes=(32,), r_max=8, S=5,
                                               dtype="f32", bad_idx_frac=0.1)
+    # two launches after the build kernel: every slot count, mostly gather
+    # groups, a long contraction (K parts with atomics), no adapter at all
+    yield "two_launches_S1024", random_problem(rng, T=5000, D=128, out_sizes=(64,), r_max=16, S=1024,
+                                                dtype="f16", bad_idx_frac=0.05)
+    yield "two_launches_groups", random_problem(rng, T=4500, D=256, out_sizes=(96, 64), r_max=32, S=400,
+                                                 dtype="bf16", with_ranks=True)
+    yield "two_launches_long_k", random_problem(rng, T=4300, D=8192, out_sizes=(64,), r_max=16, S=8,
+                                                 dtype="bf16")
+    yield "two_launches_all_base", random_problem(rng, T=4400, D=128, out_sizes=(64,), r_max=16, S=4,
+                                                   dtype="f16", idx=np.full(4400, -1, np.int32))
 
 
 @pytest.mark.parametrize("case", list(_idx_cases()), ids=lambda c: c[0])
