@@ -55,7 +55,15 @@ struct Split {
 // units clear the rows of tokens without an adapter.  With long contractions
 // gather groups are not cut into rank pieces: K parts fill the grid instead,
 // without every rank piece re-reading the group's x rows.
-template <typename Elem>
+// Tiles of several slices whose ranks are whole 16-rank blocks may instead be
+// cut across the slices: the slices' blocks taken together (TB of them) go
+// into P pieces of ceil(TB / P) blocks, P the most that fit one round of the
+// grid beside the gather groups.  When P exceeds the slice count, every unit
+// reads about the same bytes and the grid gets an even load, where per-slice
+// units would leave two units on some compute units and one on others.  (A
+// separate instance, XSL, carries this cut, so that the registers of the
+// single-slice instance stay as they are.)
+template <typename Elem, bool XSL>
 __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int use_tiles, int use_groups,
                                                             int resident, int cleared) {
   warm_args(p);
@@ -72,13 +80,23 @@ __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int
   const int n_steps = (p.D + step_elems - 1) / step_elems;
   const int64_t ns = p.n_slices;
   Split sp_t{1, 1, 1}, sp_g{1, 1, 1};
+  // cut of the tiles across slices: xsl_p pieces of xsl_nb blocks (0: none)
+  const int n_blk = p.r_max % 16 == 0 ? (int)ns * (p.r_max / 16) : 0;
+  int xsl_p = 0, xsl_nb = 0;
+  if (XSL && !cleared && ns >= 2 && n_blk > 0 && items_t > 0) {
+    const int64_t fit = min((int64_t)n_blk, ((int64_t)resident - items_g * ns) / items_t);
+    if (fit > ns) {
+      xsl_nb = (int)ceil_div((int64_t)n_blk, fit);
+      xsl_p = (int)ceil_div(n_blk, xsl_nb);
+    }
+  }
   {
     int tok_t = kTile, rk_t = p.r_max, rk_g = p.r_max;  // tokens and ranks per piece
-    int64_t u_t = items_t * ns, u_g = items_g * ns;
+    int64_t u_t = items_t * (xsl_p ? xsl_p : ns), u_g = items_g * ns;
     for (;;) {
       // candidate cuts: tiles (tokens or ranks), groups (ranks)
       const bool t_tok = tok_t > 16 && (tok_t >= rk_t || rk_t % 32 != 0);
-      const bool t_ok = u_t > 0 && (t_tok || rk_t % 32 == 0) && u_t * 2 + u_g <= resident;
+      const bool t_ok = !xsl_p && u_t > 0 && (t_tok || rk_t % 32 == 0) && u_t * 2 + u_g <= resident;
       const bool g_ok = cleared != 2 && u_g > 0 && rk_g % 32 == 0 && u_t + u_g * 2 <= resident;
       if (t_ok && (!g_ok || tok_t + rk_t >= kGroup + rk_g)) {
         if (t_tok) {
@@ -120,7 +138,7 @@ __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int
     ln = per + (xcd < rem ? 1 : 0);
   };
   int64_t st_t, ln_t, st_g, ln_g, st_z, ln_z;
-  share(n_t * ns, st_t, ln_t);
+  share(n_t * (xsl_p ? xsl_p : ns), st_t, ln_t);
   share(n_g * ns, st_g, ln_g);
   share(n_z * ns, st_z, ln_z);
   const int tid = threadIdx.x;
@@ -128,8 +146,10 @@ __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int
   for (int64_t w = lb; w < ln_t + ln_g + ln_z; w += wgs) {
     const int list = w < ln_t ? 0 : (w < ln_t + ln_g ? 1 : 2);
     int64_t unit = list == 0 ? st_t + w : (list == 1 ? st_g + (w - ln_t) : st_z + (w - ln_t - ln_g));
-    const int slice = (int)(unit % ns);
-    unit /= ns;
+    const bool xsl = xsl_p > 0 && list == 0;  // a tile unit cut across slices
+    const int per = xsl ? xsl_p : (int)ns;
+    const int slice = xsl ? 0 : (int)(unit % ns), xsl_piece = xsl ? (int)(unit % xsl_p) : 0;
+    unit /= per;
     float* vb = p.v + (int64_t)slice * p.v_slice_stride;
 
     if (list == 2) {
@@ -181,6 +201,18 @@ __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int
     const int s0 = min(n_steps, part * per_part), s1 = min(n_steps, s0 + per_part);
     const bool partial = sp.kp > 1;
     const int* utok = s_tok + tok0;
+    if (XSL && xsl) {
+      const int g0 = xsl_piece * xsl_nb, nbk = min(xsl_nb, n_blk - g0), bps = p.r_max / 16;
+      if (r > 0) {
+        contract_xsl<Elem, kRingBytes>(p, (cnt + 15) / 16, nbk, cnt, s, r, s0, s1, s_lds, utok, g0);
+      } else {
+        for (int g = g0; g < g0 + nbk; ++g)
+          clear_columns(p.v + (int64_t)(g / bps) * p.v_slice_stride, p.r_max, utok, cnt, (g % bps) * 16,
+                        (g % bps) * 16 + 16, 0, kThreads);
+      }
+      __syncthreads();  // the next unit rewrites s_tok and the rings
+      continue;
+    }
     const bool x_once = ns == 1 && sp.rs == 1;
     const int rbs = (cnt + 15) / 16;
     if (nb == 0) {
@@ -196,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void shrink_kernel(ShrinkParams p, int
 
 template <typename Elem>
 hipError_t launch(const ShrinkParams& p, bool groups, bool tiles, hipStream_t stream) {
-  const void* kernel = reinterpret_cast<const void*>(&shrink_kernel<Elem>);
+  const void* kernel = reinterpret_cast<const void*>(&shrink_kernel<Elem, false>);
   // The kernel is persistent: its grid is the workgroups the chip holds at
   // once (two per compute unit, each with four 16 KB LDS rings).  When even a
   // batch of nothing but full tiles, with every piece cut, would give fewer
@@ -213,8 +245,16 @@ hipError_t launch(const ShrinkParams& p, bool groups, bool tiles, hipStream_t st
     hipError_t e = launch_fill_zero(p.v, (int64_t)p.n_slices * p.v_slice_stride, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(shrink_kernel<Elem>, dim3(resident), dim3(kThreads), 0, stream, p, tiles ? 1 : 0,
-                     groups ? 1 : 0, resident, long_k ? 2 : (cleared ? 1 : 0));
+  // batches of several slices in whole 16-rank blocks, not cut along K: the
+  // instance that may cut tiles across slices (same grid: same LDS and
+  // occupancy)
+  const bool xsl = tiles && !cleared && p.n_slices >= 2 && p.r_max % 16 == 0;
+  if (xsl)
+    hipLaunchKernelGGL((shrink_kernel<Elem, true>), dim3(resident), dim3(kThreads), 0, stream, p, 1, groups ? 1 : 0,
+                       resident, 0);
+  else
+    hipLaunchKernelGGL((shrink_kernel<Elem, false>), dim3(resident), dim3(kThreads), 0, stream, p, tiles ? 1 : 0,
+                       groups ? 1 : 0, resident, long_k ? 2 : (cleared ? 1 : 0));
   return hipGetLastError();
 }
 

@@ -145,10 +145,14 @@ __device__ inline void clear_columns(float* vb, int r_max, const int* s_tok, int
 // columns whole (zeros past the rank).  XONCE: no other unit reads this
 // unit's x rows (one slice, no rank pieces), so they are loaded with a
 // non-temporal hint and do not displace reused data from the caches.
-template <typename Elem, int RB, int NB, bool XONCE, int RING>
+// XSL: the rank blocks run across slices -- block nb is block g0 + nb of the
+// slices' 16-rank blocks taken together (slice (g0 + nb) / (r_max / 16)),
+// `slice`, c_lo and c_hi are unused, r >= 1, and the unit stores its blocks'
+// columns whole (zeros past the rank); not with `partial` or `part`.
+template <typename Elem, int RB, int NB, bool XONCE, int RING, bool XSL = false>
 __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, int s, int r, int slice, int s0,
                                               int s1, bool partial, float* part, char* s_lds, const int* s_tok,
-                                              int c_lo, int c_hi) {
+                                              int c_lo, int c_hi, int g0 = 0) {
   using M = StepMma<Elem>;
   constexpr int kVec = Traits<Elem>::kVec;
   constexpr int kStep = 4 * kVec;  // elements per K step (64 bytes)
@@ -173,9 +177,20 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
   // 16-byte piece (l % 8) ^ (l / 8) of the batch's line of that row, and lands
   // at byte 16 l of the load's 1 KB.
   const char* xb = reinterpret_cast<const char*>(p.x);
-  const char* ab = reinterpret_cast<const char*>(p.A[slice]) +
-                   ((int64_t)s * p.r_max + c_lo) * p.D * (int64_t)sizeof(Elem);
-  const int r_loc = min(r, c_hi) - c_lo;  // rank rows of this unit, >= 1
+  const char* ab = reinterpret_cast<const char*>(p.A[XSL ? 0 : slice]) +
+                   ((int64_t)s * p.r_max + (XSL ? 0 : c_lo)) * p.D * (int64_t)sizeof(Elem);
+  const int r_loc = XSL ? r : min(r, c_hi) - c_lo;  // rank rows of this unit, >= 1
+  // XSL: each rank block's slice, A base and first rank
+  const int bps = p.r_max / 16;
+  const char* abk[NB];
+  int bsl[NB], bcol[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    bsl[nb] = XSL ? (g0 + nb) / bps : slice;
+    bcol[nb] = XSL ? ((g0 + nb) % bps) * 16 : nb * 16;  // XSL: the slot's rank; else relative to c_lo
+    abk[nb] = XSL ? reinterpret_cast<const char*>(p.A[bsl[nb]]) + (int64_t)s * p.r_max * p.D * (int64_t)sizeof(Elem)
+                  : ab;
+  }
   const int t0 = s_tok[0];  // cnt >= 1: a valid token
   const uint32_t piece = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
   uint32_t so[NBLK][2];
@@ -189,7 +204,7 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int k = nb * 16 + row;
+      const int k = bcol[nb] + row;
       so[RB + nb][q] = (uint32_t)((int64_t)(k < r_loc ? k : r_loc - 1) * p.D * (int64_t)sizeof(Elem)) + piece;
     }
   }
@@ -218,7 +233,8 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         if (XONCE && bk < RB) load_to_lds_nt(xb, so[bk][q] + boff, dst + (uint32_t)(bk * kBlockBytes + q * 1024));
-        else load_to_lds(bk < RB ? xb : ab, so[bk][q] + boff, dst + (uint32_t)(bk * kBlockBytes + q * 1024));
+        else load_to_lds(bk < RB ? xb : abk[bk < RB ? 0 : bk - RB], so[bk][q] + boff,
+                         dst + (uint32_t)(bk * kBlockBytes + q * 1024));
   };
   int issued = 0;
   for (; issued < my_n && issued < DEPTH; ++issued) issue(issued);
@@ -264,8 +280,8 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int k = nb * 16 + m;
-        const char* row = ab + (int64_t)(k < r_loc ? k : r_loc - 1) * p.D * (int64_t)sizeof(Elem);
+        const int k = bcol[nb] + m;
+        const char* row = abk[nb] + (int64_t)(k < r_loc ? k : r_loc - 1) * p.D * (int64_t)sizeof(Elem);
         op[RB + nb] = ld16_or0(row + (ok ? (int64_t)d * (int64_t)sizeof(Elem) : 0), ok);
       }
 #pragma unroll
@@ -300,7 +316,17 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
       a[3] += o[3];
     }
     // lane (m, kg) holds D[token rb*16 + 4 kg + i][rank c_lo + nb*16 + m]
-    const int k = c_lo + nb * 16 + m;
+    // (XSL: rank bcol[nb] + m of slice bsl[nb])
+    const int k = (XSL ? 0 : c_lo) + bcol[nb] + m;
+    if constexpr (XSL) {
+      float* vs = p.v + (int64_t)bsl[nb] * p.v_slice_stride;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = s_tok[rb * 16 + 4 * kg + i];
+        if (t >= 0) vs[(int64_t)t * p.r_max + k] = k < r ? a[i] * sc : 0.f;
+      }
+      continue;
+    }
     if (part) {
       // raw sums (unscaled) into the unit's slab, row = token position, as
       // device-coherent stores (another workgroup, on any XCD, reads them)
@@ -321,7 +347,8 @@ __device__ __forceinline__ void contract_unit(const ShrinkParams& p, int cnt, in
       }
     }
   }
-  if (!partial && !part) clear_columns(vb, p.r_max, s_tok, cnt, min(c_lo + NB * 16, c_hi), c_hi, 0, kUnitThreads);
+  if (!XSL && !partial && !part)
+    clear_columns(vb, p.r_max, s_tok, cnt, min(c_lo + NB * 16, c_hi), c_hi, 0, kUnitThreads);
 }
 
 template <typename Elem, int RB, bool XONCE, int RING>
@@ -333,6 +360,26 @@ __device__ __forceinline__ void contract_rb(const ShrinkParams& p, int nb, int c
     case 3: contract_unit<Elem, RB, 3, XONCE, RING>(p, cnt, s, r, slice, s0, s1, partial, part, s_lds, s_tok, c_lo, c_hi); break;
     default: contract_unit<Elem, RB, 4, XONCE, RING>(p, cnt, s, r, slice, s0, s1, partial, part, s_lds, s_tok, c_lo, c_hi); break;
   }
+}
+
+// An XSL unit (rank blocks across slices, see contract_unit): rbs token blocks
+// by nb rank blocks from block g0.
+template <typename Elem, int RB, int RING>
+__device__ __forceinline__ void contract_xsl_rb(const ShrinkParams& p, int nb, int cnt, int s, int r, int s0, int s1,
+                                                char* s_lds, const int* s_tok, int g0) {
+  switch (nb) {
+    case 1: contract_unit<Elem, RB, 1, false, RING, true>(p, cnt, s, r, 0, s0, s1, false, nullptr, s_lds, s_tok, 0, 0, g0); break;
+    case 2: contract_unit<Elem, RB, 2, false, RING, true>(p, cnt, s, r, 0, s0, s1, false, nullptr, s_lds, s_tok, 0, 0, g0); break;
+    case 3: contract_unit<Elem, RB, 3, false, RING, true>(p, cnt, s, r, 0, s0, s1, false, nullptr, s_lds, s_tok, 0, 0, g0); break;
+    default: contract_unit<Elem, RB, 4, false, RING, true>(p, cnt, s, r, 0, s0, s1, false, nullptr, s_lds, s_tok, 0, 0, g0); break;
+  }
+}
+template <typename Elem, int RING>
+__device__ __forceinline__ void contract_xsl(const ShrinkParams& p, int rbs, int nb, int cnt, int s, int r, int s0,
+                                             int s1, char* s_lds, const int* s_tok, int g0) {
+  if (rbs == 1) contract_xsl_rb<Elem, 1, RING>(p, nb, cnt, s, r, s0, s1, s_lds, s_tok, g0);
+  else if (rbs == 2) contract_xsl_rb<Elem, 2, RING>(p, nb, cnt, s, r, s0, s1, s_lds, s_tok, g0);
+  else contract_xsl_rb<Elem, 4, RING>(p, nb, cnt, s, r, s0, s1, s_lds, s_tok, g0);
 }
 
 template <typename Elem, bool XONCE, int RING>

@@ -76,6 +76,24 @@ def edge_problems():
                            dtype=dtype, idx=idx, with_ranks=True)
         p.ranks[:] = rng.integers(1, 65, 24)
         yield f"pieces_{dtype}", p, "auto"
+    for dtype, n_sl, r_max in (("bf16", 3, 64), ("f16", 2, 32), ("f16", 3, 32), ("bf16", 2, 64)):
+        # >= 4096 tokens, two or three slices of rank 32 or 64, 16-bit (the
+        # shape of fused q/k/v and gate/up prefill): ragged tiles, gather
+        # groups beside them, a K tail (D = 520 is not a whole number of
+        # 64-element batches), strided x rows, mixed ranks with one slot of
+        # rank 0, base tokens.
+        counts = [900, 700, 651, 500, 480, 64, 63, 48, 47, 20, 5, 1]
+        idx = np.concatenate([np.repeat(np.arange(12), counts), np.full(700, -1)]).astype(np.int32)
+        rng.shuffle(idx)
+        p = random_problem(rng, T=idx.size, D=520, out_sizes=(64, 32, 48)[:n_sl], r_max=r_max, S=12,
+                           dtype=dtype, idx=idx, with_ranks=True, ldx=528)
+        p.ranks[:] = rng.integers(1, r_max + 1, 12)
+        p.ranks[4] = 0
+        yield f"large_slices{n_sl}_r{r_max}_{dtype}", p, "auto"
+    # the same with a longer contraction and a tail
+    yield "large_slices3_long_K", random_problem(
+        rng, T=4100, D=2056, out_sizes=(128, 64, 64), r_max=64, S=3, dtype="bf16",
+        with_ranks=True), "auto"
     for mode in ("auto", "bgmv", "sgmv"):
         # long segments (>= 48 tokens go to the segmented path in auto mode)
         idx = np.repeat(np.arange(5, dtype=np.int32), [200, 64, 63, 1, 130])
