@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kMaskThreads, 2) void mask_expand_kernel(MaskParams
     for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < kMaxQ; ++q) {
-      if (q >= nq) break;  // uniform
+      if (q >= nq) continue;  // uniform; predicated so that the loop unrolls
       const int c = q * kStep + kg * kVec;
       const int s_c = c / p.r_max, within = c - s_c * p.r_max;
       const int r_c = s_c < p.S ? slot_rank(p.ranks, s_c, p.r_max) : 0;

@@ -118,10 +118,12 @@ __global__ __launch_bounds__(kWThreads) void build_segments_wide_kernel(const in
   int bad = 0;
   for (int c0 = wave; c0 < n_chunks; c0 += kWWaves * kWBatch) {
     if (c0 != wave) load_batch(c0);
+    // predicated rather than left early, so that the loop unrolls and each
+    // chunk waits only for its own load
 #pragma unroll
     for (int u = 0; u < kWBatch; ++u) {
       const int c = c0 + u * kWWaves;
-      if (c >= n_chunks) break;  // uniform
+      if (c >= n_chunks) continue;  // uniform
       const bool valid = c * 64 + lane < T;
       const int k = valid ? key_of(raw[u]) : S;
       if (valid && raw[u] != -1 && k == S) bad = 1;
