@@ -716,7 +716,8 @@ def main():
         err_y=head.get("err_y"), err_v=head.get("err_v"), meta_bitexact=head.get("meta_bitexact"),
         workspace_errors=head.get("workspace_errors"),
         calls=head.get("calls"),
-        noop=head.get("noop"),
+        # the all-base batch's overhead next to the base layer (its own config)
+        noop=head.get("noop") or (configs or {}).get("zipf_many_noop", {}).get("noop"),
         roofline=roofline,
         cpu_baseline=cpu,
         configs=configs,
