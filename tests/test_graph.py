@@ -38,7 +38,7 @@ def _specified(seg, T, S):
         rec[off["tiles"]:off["tiles"] + 68 * info[5]]])
 
 
-@pytest.mark.parametrize("name", ["tiny_bgmv", "decode_qproj", "mixed_rank_mlp", "zipf_many"])
+@pytest.mark.parametrize("name", ["tiny_bgmv", "decode_qproj", "mixed_rank_mlp", "zipf_many", "prefill_qkv"])
 def test_graph_replays_match_eager(name):
     wl = make_workload(name)
     say(f"[graph] {name} T={wl.T} S={wl.S} replays={REPLAYS}")
