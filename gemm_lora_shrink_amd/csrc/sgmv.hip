@@ -32,6 +32,7 @@ constexpr int kSubs = kTile / 16;                              // 16-token sub-b
 constexpr int kVRow = LORA_MAX_RANK + 8;                       // padded 16-bit LDS row of v
 constexpr int kTileRun = 2;              // column tiles per unit of a segmented tile (see the kernel)
 constexpr int kGroupRun = 4 * kTileRun;  // ... of a gather group
+constexpr int kBStage = kExpandColsPerWave * 8;  // 16-byte pieces of one wave's B rows of a tile (64 rows x 128 B)
 
 // One tile unit: the column tiles [ct_begin, ct_end) of an item of up to 64
 // tokens (NSUB 16-token sub-blocks; sub-blocks past the item's tokens hold no
@@ -44,7 +45,7 @@ constexpr int kGroupRun = 4 * kTileRun;  // ... of a gather group
 template <typename Elem, int NSUB, int RUN>
 __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, int* s_tok, float* s_unscale,
                                    Elem (*s_vhi)[kVRow], Elem (*s_vlo)[kVRow], float (*s_tr)[16][kTrRow],
-                                   int slice, int s, int r, int out, int ct_begin, int ct_end) {
+                                   u32x4* s_bw, int slice, int s, int r, int out, int ct_begin, int ct_end) {
   using M = Mfma<Elem>;
   using V = typename M::vec;
   using Tr = Traits<Elem>;
@@ -86,24 +87,26 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
         dst[sb][h] = ld16_or0_nt(ok ? ybase + jw + (int64_t)t * p.ldy : yzero, ok);
       }
   };
-  // A operand: this wave's 64 B rows of column tile `ct` (4 blocks x 16), both
-  // rank steps; rank columns past the slot's rank are not read (zeros past
-  // ct_end: the last prefetch issues only loads of the zero constant)
-  auto load_b = [&](int ct, u32x4 (&bop)[4][2]) {
+  // A operand: this wave's 64 B rows of column tile `ct`, loaded in whole
+  // lines -- lane l takes the 16-byte piece l % 8 of row 8 i + l / 8, i = 0..7
+  // (the MFMA layout would have every 16 lanes touch 16 rows, which a compute
+  // unit streams far more slowly) -- and moved into MFMA layout through the
+  // wave's LDS block before the tile's products.  Pieces past the slot's rank
+  // and rows past `out` are not read (zeros past ct_end: the last prefetch
+  // issues only loads of the zero constant).
+  const int bl_row = lane >> 3, bl_piece = lane & 7;
+  auto load_b = [&](int ct, u32x4 (&bl)[8]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int row = jw + cb * 16 + n;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int k0 = ks * 32 + kg * 8;
-        const bool ok = ct < ct_end && ks < nks && row < out && k0 < r;
-        bop[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * ldb + k0 : 0), ok);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int row = jw + 8 * i + bl_row;
+      const int k0 = bl_piece * 8;
+      const bool ok = ct < ct_end && row < out && k0 < r;
+      bl[i] = ld16_or0(Bs + (ok ? (int64_t)row * ldb + k0 : 0), ok);
     }
   };
   u32x4 yold[NSUB][2];
-  u32x4 bop[4][2];
+  u32x4 bop[8];
   load_y(ct_begin, yold);
   load_b(ct_begin, bop);
 
@@ -148,17 +151,30 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
   lds_barrier();  // the v operands are visible; y and B loads stay in flight
 
   // one column tile with its y and B rows (loaded one tile ahead)
-  auto compute_tile = [&](int ct, const u32x4 (&ycur)[NSUB][2], const u32x4 (&bcur)[4][2]) {
+  auto compute_tile = [&](int ct, const u32x4 (&ycur)[NSUB][2], const u32x4 (&bcur)[8]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
     const bool ycol_ok = jw + yc < out;  // out is a multiple of 8
+    // the B lines into MFMA layout: row q's piece c sits at piece c ^ (q % 8)
+    // of the row's 128 bytes in the wave's block (conflict-free both ways)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = 8 * i + bl_row;
+      s_bw[q * 8 + (bl_piece ^ (q & 7))] = bcur[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // a rank that is not a multiple of 8 ends inside one 16-byte piece: zero
     // the columns past it (loaded pieces past the rank are zeros already)
     V bv[4][2];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        bv[cb][ks] = as_vec<V>(ragged_rank ? mask_tail16(bcur[cb][ks], ks * 32 + kg * 8, r) : bcur[cb][ks]);
+      for (int ks = 0; ks < 2; ++ks) {
+        const int q = cb * 16 + n, c = ks * 4 + kg;
+        const u32x4 b = s_bw[q * 8 + (c ^ (q & 7))];
+        bv[cb][ks] = as_vec<V>(ragged_rank ? mask_tail16(b, ks * 32 + kg * 8, r) : b);
+      }
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
       if (sb >= n_sub) break;
@@ -216,7 +232,7 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
 
   // two tiles per iteration, so that the register buffers alternate without
   // copies; the next tile's y and B rows are in flight during each tile
-  u32x4 ynext[NSUB][2], bnext[4][2];
+  u32x4 ynext[NSUB][2], bnext[8];
 #pragma unroll
   for (int i = 0; i < RUN; i += 2) {
     const int ct = ct_begin + i;
@@ -261,7 +277,8 @@ __device__ inline UnitWords load_unit_words(const ExpandParams& p, bool tiles, i
 template <typename Elem>
 __device__ inline void expand_unit(const ExpandParams& p, int slice, bool tiles, const UnitWords& w, int ct_begin,
                                    int ct_end, const int* s_rank, int* s_tok, float* s_unscale,
-                                   Elem (*s_vhi)[kVRow], Elem (*s_vlo)[kVRow], float (*s_tr)[16][kTrRow]) {
+                                   Elem (*s_vhi)[kVRow], Elem (*s_vlo)[kVRow], float (*s_tr)[16][kTrRow],
+                                   u32x4 (*s_b)[kBStage]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int n = lane & 15, yr = lane >> 3;
@@ -295,7 +312,7 @@ __device__ inline void expand_unit(const ExpandParams& p, int slice, bool tiles,
     return;
   }
   expand_tile<Elem, kSubs, kTileRun>(p, tok(tid >> 2, tw_v), (it.cnt + 15) >> 4, s_tok, s_unscale, s_vhi, s_vlo, s_tr,
-                           slice, s, r, out, ct_begin, ct_end);
+                                     s_b[tid >> 6], slice, s, r, out, ct_begin, ct_end);
   lds_barrier();  // the next unit rewrites s_tok and the v operands
 }
 
@@ -326,6 +343,7 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_expand_kernel(ExpandParams p
   __shared__ __attribute__((aligned(16))) Elem s_vhi[kTile][kVRow];
   __shared__ __attribute__((aligned(16))) Elem s_vlo[kTile][kVRow];
   __shared__ __attribute__((aligned(16))) float s_tr[4][16][kTrRow];
+  __shared__ u32x4 s_b[4][kBStage];  // per wave: one tile's B rows on their way to MFMA layout
 
   const int64_t n_g = use_groups ? record_items(p.rec, p.T, p.S, false) : 0;
   const int64_t n_t = use_tiles ? record_items(p.rec, p.T, p.S, true) : 0;
@@ -378,7 +396,8 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_expand_kernel(ExpandParams p
     const Unit nxt = decode(u + G);
     UnitWords nw{};
     if (nxt.ok) nw = load_unit_words(p, nxt.tiles, nxt.item);
-    expand_unit<Elem>(p, cur.slice, cur.tiles, cw, cur.ct0, cur.ct1, s_rank, s_tok, s_unscale, s_vhi, s_vlo, s_tr);
+    expand_unit<Elem>(p, cur.slice, cur.tiles, cw, cur.ct0, cur.ct1, s_rank, s_tok, s_unscale, s_vhi, s_vlo, s_tr,
+                      s_b);
     cur = nxt;
     cw = nw;
   }
