@@ -383,7 +383,7 @@ def run_config(name, args, torch, glsa, dev, copy_gbs, headline):
     active = bool(np.any((wl.idx >= 0) & (wl.idx < S)))
     fused = args.path == "fused"
     is16 = wl.dtype in ("f16", "bf16")
-    one_launch = fused and is16 and T <= glsa.fused_max_tokens()
+    one_launch = fused and T <= glsa.fused_max_tokens_for(wl.dtype)
     # the first layer's call builds the record inside its one launch
     build_in_call = (one_launch and not args.separate_build and active and problems[0].timed_expand
                      and S <= 256)

@@ -88,6 +88,8 @@ def _load():
     lib.lora_expand.restype = ctypes.c_int
     lib.lora_fused_max_tokens.argtypes = []
     lib.lora_fused_max_tokens.restype = i32
+    lib.lora_fused_max_tokens_for.argtypes = [i32]
+    lib.lora_fused_max_tokens_for.restype = i32
     lib.lora_shrink_expand_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.lora_shrink_expand_workspace_bytes.restype = sz
     lib.lora_shrink_expand.argtypes = [ctypes.c_int, vp, i64, i32, i32, i32, vp, vp, vp, vp, i32,
@@ -337,6 +339,14 @@ def apply(x, A, B, y, seg, out_offsets, *, scale=None, ranks=None, v=None, activ
 
 def fused_max_tokens():
     return int(_load().lora_fused_max_tokens())
+
+
+def fused_max_tokens_for(dtype):
+    """Largest T that shrink_expand runs as one launch for data of `dtype`
+    (a torch dtype, or one of "f32", "f16", "bf16")."""
+    codes = {"f32": 0, "f16": 1, "bf16": 2}
+    code = codes[dtype] if isinstance(dtype, str) else _DTYPES[dtype]
+    return int(_load().lora_fused_max_tokens_for(code))
 
 
 def workspace_bytes(T, S, n_slices, r_max):

@@ -138,6 +138,15 @@ LORA_EXPORT int32_t lora_sgmv_min_tokens(void) { return kSgmvMinTokens; }
 
 LORA_EXPORT int32_t lora_fused_max_tokens(void) { return kFusedMaxTokens; }
 
+LORA_EXPORT int32_t lora_fused_max_tokens_for(lora_dtype dt) {
+  switch (dt) {
+    case LORA_F32: return kF32FusedMaxTokens;
+    case LORA_F16:
+    case LORA_BF16: return kFusedMaxTokens;
+  }
+  return 0;
+}
+
 LORA_EXPORT size_t lora_segments_bytes(int32_t T, int32_t S) {
   if (T < 0 || S < 1 || S > LORA_MAX_SLOTS) return 0;
   const SegLayout L = seg_layout(T, S);
@@ -366,7 +375,7 @@ lora_status shrink_expand_impl(lora_dtype dt, const void* x, int64_t ldx, int32_
   *ran = e == hipSuccess;
   // one launch only where all of its workgroups are resident at once (its
   // consumers wait for its producers); otherwise the separate launches
-  const bool one_launch = dt != LORA_F32 && T <= kFusedMaxTokens &&
+  const bool one_launch = T <= lora_fused_max_tokens_for(dt) &&
                           fused_coresident(dt, T, idx != nullptr && S <= kFusedBuildMaxSlots);
   if (e != hipSuccess) {
   } else if (one_launch && idx && S <= kFusedBuildMaxSlots) {

@@ -17,6 +17,7 @@ constexpr int kGroup = 16;  // tokens per gather (BGMV) work item
 constexpr int kTile = 64;   // tokens per segmented (SGMV) work item
 constexpr int kSgmvMinTokens = 48;  // AUTO: slots with this many tokens go to SGMV
 constexpr int kFusedMaxTokens = 4096;  // lora_shrink_expand runs as one launch up to this T
+constexpr int kF32FusedMaxTokens = 2048;  // ... and fp32 batches up to this T
 constexpr int kFusedBuildMaxSlots = 256;  // ... and builds the record inside that launch up to this S
 constexpr int kMaskMaxLanes = 128;  // the mask form takes adapters of at most this many stacked ranks (S * r_max)
 

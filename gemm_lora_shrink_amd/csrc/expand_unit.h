@@ -198,6 +198,74 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const VSrc& vs
   }
 }
 
+// The same group expand for fp32 data, on the vector ALUs: v is fp32 already
+// and the products are plain fp32 FMAs (a 16x16 block of rank 64 would take
+// sixteen 16x16x4 fp32 matrix instructions).  The wave puts the group's v rows
+// (from vsrc, in the lane layout above) and its tokens (lane n's tok_n) into
+// its LDS block s_v; per 256-column tile each lane then owns one of the wave's
+// 64 columns: it reads that column's B row over the rank, forms the 16 tokens'
+// dot products against the v rows (LDS broadcasts) and read-modify-writes y
+// once per element.
+template <typename VSrc>
+__device__ inline void expand_group_f32(const ExpandParams& p, const VSrc& vsrc, int tok_n, float (*s_v)[kTrRow],
+                                        int slice, int s, int r, int out, int ct_begin, int ct_end) {
+  static_assert(kTrRow >= LORA_MAX_RANK + 1, "a v row and a token word fit a block row");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  f32x4 vraw[2][2];
+  vsrc(vraw);  // lane (n, kg): v[token n][32 ks + 8 kg .. + 7], zeros past the rank
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) *reinterpret_cast<f32x4*>(&s_v[n][ks * 32 + kg * 8 + 4 * h]) = vraw[ks][h];
+  if (kg == 0) s_v[n][LORA_MAX_RANK] = __int_as_float(tok_n);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int tk[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) tk[t] = __float_as_int(s_v[t][LORA_MAX_RANK]);
+  const float* Bs = reinterpret_cast<const float*>(p.B[slice]) + (int64_t)s * out * p.r_max;
+  const int ldb = b_row_stride(p, r);
+  float* ybase = reinterpret_cast<float*>(p.y) + p.out_off[slice];
+  const float* yzero = reinterpret_cast<const float*>(g_zero16);
+  for (int ct = ct_begin; ct < ct_end; ++ct) {
+    const int col = ct * kExpandColsPerWG + wave * kExpandColsPerWave + lane;
+    const bool col_ok = col < out;
+    // the tile's y values first, so that their loads are in flight together
+    float yv[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const bool ok = col_ok && tk[t] >= 0;
+      yv[t] = *(ok ? ybase + (int64_t)tk[t] * p.ldy + col : yzero);
+    }
+    float acc[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) acc[t] = 0.f;
+    const float* brow = Bs + (int64_t)(col_ok ? col : 0) * ldb;
+    for (int k0 = 0; k0 < r; k0 += 4) {  // rows hold whole 16-byte pieces up to the rank
+      f32x4 b = ldf4_or0(brow + k0, col_ok);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = k0 + i < r ? b[i] : 0.f;  // padding past the rank is not read as data
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(&s_v[t][k0]);
+        acc[t] = __builtin_fmaf(b[0], v4[0], acc[t]);
+        acc[t] = __builtin_fmaf(b[1], v4[1], acc[t]);
+        acc[t] = __builtin_fmaf(b[2], v4[2], acc[t]);
+        acc[t] = __builtin_fmaf(b[3], v4[3], acc[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (col_ok && tk[t] >= 0) ybase[(int64_t)tk[t] * p.ldy + col] = yv[t] + acc[t];
+  }
+  // the block is rewritten by the wave's next unit only after these reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace
 
 }  // namespace lora

@@ -495,7 +495,10 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
         }
       }
     };
-    expand_group_direct<Elem>(e, vsrc, ytok0, ytok1, s_tr, sl, s, r, (int)e.out_size[sl], ct_begin, ct_end);
+    if constexpr (sizeof(Elem) == 4)
+      expand_group_f32(e, vsrc, tok_n, s_tr[wave], sl, s, r, (int)e.out_size[sl], ct_begin, ct_end);
+    else
+      expand_group_direct<Elem>(e, vsrc, ytok0, ytok1, s_tr, sl, s, r, (int)e.out_size[sl], ct_begin, ct_end);
     // this unit's column tiles are counted as consumed (after its y stores are
     // issued, so the atomic's round trip overlaps them); the last consumer of
     // the chunk sets the counter back to zero for the next call
@@ -557,6 +560,9 @@ FusedLayout fused_layout(int64_t bytes) {
 bool fused_coresident(lora_dtype dt, int32_t T, bool from_idx) {
   const int tpt = !from_idx ? 0 : (T <= kTokPerThreadSmall * kFThreads ? kTokPerThreadSmall : kTokPerThreadLarge);
   switch (dt) {
+    case LORA_F32:  // fp32: the record form and the idx form of at most 8 tokens per thread
+      return T <= kF32FusedMaxTokens &&
+             (tpt == 0 ? fused_fits<float, 0>() : fused_fits<float, kTokPerThreadSmall>());
     case LORA_F16:
       return tpt == 0 ? fused_fits<half_t, 0>()
                       : tpt == kTokPerThreadSmall ? fused_fits<half_t, kTokPerThreadSmall>()
@@ -591,6 +597,9 @@ hipError_t launch_fused(lora_dtype dt, const ShrinkParams& sp, const ExpandParam
   // record form, or the idx form with at most 8 or 16 tokens per thread
   const int tpt = idx == nullptr ? 0 : (sp.T <= kTokPerThreadSmall * kFThreads ? kTokPerThreadSmall : kTokPerThreadLarge);
   switch (dt) {
+    case LORA_F32:
+      if (sp.T > kF32FusedMaxTokens) return hipErrorInvalidValue;
+      return tpt == 0 ? fused_launch<float, 0>(f, stream) : fused_launch<float, kTokPerThreadSmall>(f, stream);
     case LORA_F16:
       return tpt == 0 ? fused_launch<half_t, 0>(f, stream)
                       : tpt == kTokPerThreadSmall ? fused_launch<half_t, kTokPerThreadSmall>(f, stream)

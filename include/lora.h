@@ -268,11 +268,12 @@ lora_status lora_expand(lora_dtype dt, const float *v, int64_t v_slice_stride, i
  *              number of polls, so a call always ends; the environment
  *              variable LORA_MI355X_FUSED_SPIN_LIMIT, when set, lowers that
  *              bound (for tests of the give-up path).
- * fp16/bf16 batches of T <= lora_fused_max_tokens() run as one launch:
- * producer work units shrink 16-token chunks over ranges of D into the
- * workspace and consumer units expand each chunk once every part of it is
- * there.  Larger batches and fp32 run as the shrink launch and the expand
- * launch, with v in the workspace when v is NULL.
+ * Batches of T <= lora_fused_max_tokens_for(dt) run as one launch (4096
+ * tokens for fp16/bf16, 2048 for fp32): producer work units shrink 16-token
+ * chunks over ranges of D into the workspace and consumer units expand each
+ * chunk once every part of it is there (fp32 chunks on the vector ALUs).
+ * Larger batches run as the shrink launch and the expand launch, with v in
+ * the workspace when v is NULL.
  * Co-residency.  The one launch's consumers wait for its producers, so it
  * needs every one of its workgroups on the device at once: its grid is what
  * the current device holds at once (rounded down to a multiple of 8), and
@@ -291,6 +292,9 @@ size_t lora_shrink_expand_workspace_bytes(int32_t T, int32_t S, int32_t n_slices
 
 /* Largest T that lora_shrink_expand runs as one launch (16-bit data). */
 int32_t lora_fused_max_tokens(void);
+
+/* The same for data of type dt (0 for an unknown dt). */
+int32_t lora_fused_max_tokens_for(lora_dtype dt);
 
 lora_status lora_shrink_expand(lora_dtype dt, const void *x, int64_t ldx, int32_t T, int32_t D,
                                int32_t n_slices, const void *const *A, const void *const *B,

@@ -56,7 +56,7 @@ def run_fused(p, d, seg, ws=None, from_idx=False):
                        idx=d["idx"] if from_idx else None)
     torch.cuda.synchronize()
     assert glsa.workspace_errors(ws) == 0, "a fused wait gave up"
-    if p.dtype != "f32" and p.T > 0:
+    if p.T > 0:
         assert not torch.any(ws[:fused_counter_bytes(ws)]).item(), "fused counters not back at zero"
     return v
 

@@ -76,7 +76,13 @@ def _idx_cases():
                                             dtype="bf16")
     yield "two_launches_T4200", random_problem(rng, T=4200, D=256, out_sizes=(128,), r_max=16, S=40,
                                                dtype="f16")
-    yield "fp32_two_launches", random_problem(rng, T=200, D=64, out_sizes=(32,), r_max=8, S=5,
+    # fp32: one launch up to 2048 tokens (chunks expanded on the vector ALUs,
+    # per-slot ranks that are not multiples of 4), two launches past it
+    yield "fp32_one_launch", random_problem(rng, T=200, D=64, out_sizes=(32, 300), r_max=8, S=5,
+                                            dtype="f32", bad_idx_frac=0.1, with_ranks=True)
+    yield "fp32_one_launch_T2048", random_problem(rng, T=2048, D=96, out_sizes=(520,), r_max=64, S=20,
+                                                  dtype="f32", with_ranks=True)
+    yield "fp32_two_launches", random_problem(rng, T=2100, D=64, out_sizes=(32,), r_max=8, S=5,
                                               dtype="f32", bad_idx_frac=0.1)
     # two launches after the build kernel: every slot count, mostly gather
     # groups, a long contraction (K parts with atomics), no adapter at all

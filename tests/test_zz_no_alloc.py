@@ -74,11 +74,12 @@ def test_noalloc_matches_workspace_call_twice(from_idx):
 
 
 def test_noalloc_two_launch_forms():
-    """fp32 data and a batch past the one-launch limit run as separate
-    launches on the scratch (v kept in it when the caller passes none)."""
+    """Batches past the one-launch limits (4096 tokens of 16-bit data, 2048
+    of fp32) run as separate launches on the scratch (v kept in it when the
+    caller passes none)."""
     rng = np.random.default_rng(6)
     cases = [random_problem(rng, T=4200, D=256, out_sizes=(128,), r_max=16, S=40, dtype="f16"),
-             random_problem(rng, T=90, D=128, out_sizes=(64,), r_max=8, S=5, dtype="f32")]
+             random_problem(rng, T=2100, D=128, out_sizes=(64,), r_max=8, S=5, dtype="f32")]
     for p in cases:
         say(f"[noalloc] two launches: T={p.T} dtype={p.dtype}")
         (y_ws, _), (y_na, v_na) = _both(p, from_idx=True)
@@ -108,3 +109,18 @@ def test_noalloc_refuses_calls_past_the_scratch():
     assert e.value.status == glsa.LORA_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.equal(d["y"].view(torch.int16), y0.view(torch.int16))
+
+
+def test_noalloc_fp32_one_launch():
+    """fp32 batches of up to 2048 tokens run as the one launch too (their
+    chunks expanded on the vector ALUs), here on the scratch, in both forms."""
+    rng = np.random.default_rng(8)
+    p = random_problem(rng, T=300, D=128, out_sizes=(96,), r_max=16, S=6, dtype="f32", with_ranks=True)
+    v_ref, y_ref = oracle_ref(p)
+    for from_idx in (False, True):
+        say(f"[noalloc] fp32 one launch: T={p.T} {'idx' if from_idx else 'record'} form")
+        (y_ws, v_ws), (y_na, v_na) = _both(p, from_idx)
+        assert rel_err(oracle.decode(y_na, p.dtype), y_ref) <= Y_TOL[p.dtype]
+        assert rel_err(v_na, v_ref) <= V_TOL
+        assert np.array_equal(y_na, y_ws), "fp32: y differs from lora_shrink_expand's"
+        assert np.array_equal(v_na, v_ws), "fp32: v differs from lora_shrink_expand's"
