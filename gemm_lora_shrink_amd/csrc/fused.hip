@@ -436,7 +436,8 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
       if (write_v && tok_n >= 0)
         for (int k0 = kg * 8; k0 < r_max; k0 += 32) {
           *reinterpret_cast<f32x4*>(vrow + k0) = f32x4{0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<f32x4*>(vrow + k0 + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+          // fp32 rows may end halfway through a piece of 8 (r_max a multiple of 4)
+          if (k0 + 4 < r_max) *reinterpret_cast<f32x4*>(vrow + k0 + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       continue;
     }
@@ -470,10 +471,12 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
             f32x4 w[kSumBatch][2];
 #pragma unroll
             for (int j = 0; j < kSumBatch; ++j) {
-              const bool okq = ok && q0 + j < kp;
+              // the second half of the piece only below the rank: an fp32
+              // row (r_max a multiple of 4) may end after the first
+              const bool okq = ok && q0 + j < kp, okq1 = okq && k0 + 4 < r;
               const float* src = slabs + (okq ? (q0 + j) * slab_floats + k0 : 0);
               w[j][0] = ldf4_or0(src, okq);
-              w[j][1] = ldf4_or0(src + 4, okq);
+              w[j][1] = ldf4_or0(src + (okq1 ? 4 : 0), okq1);
             }
 #pragma unroll
             for (int j = 0; j < kSumBatch; ++j) {
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(kFThreads, 2) void fused_kernel(FusedParams f) {
         vraw[ks][1] = a1;
         if (write_v && tok_n >= 0 && k0 < r_max) {
           *reinterpret_cast<f32x4*>(vrow + k0) = a0;
-          *reinterpret_cast<f32x4*>(vrow + k0 + 4) = a1;
+          if (k0 + 4 < r_max) *reinterpret_cast<f32x4*>(vrow + k0 + 4) = a1;
         }
       }
     };

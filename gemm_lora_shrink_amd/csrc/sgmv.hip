@@ -302,9 +302,10 @@ __device__ inline void expand_unit(const ExpandParams& p, int slice, bool tiles,
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int k0 = ks * 32 + kg * 8;
-        const bool ok = tok_n >= 0 && ks < nks && k0 < r;
+        // an fp32 row (r_max a multiple of 4) may end halfway through the piece
+        const bool ok = tok_n >= 0 && ks < nks && k0 < r, ok1 = ok && k0 + 4 < r;
         vraw[ks][0] = ldf4_or0(vrow + (ok ? k0 : 0), ok);
-        vraw[ks][1] = ldf4_or0(vrow + (ok ? k0 + 4 : 0), ok);
+        vraw[ks][1] = ldf4_or0(vrow + (ok1 ? k0 + 4 : 0), ok1);
       }
     };
     expand_group_direct<Elem>(p, vsrc, tok(yr, tw_y0), tok(yr + 8, tw_y1), s_tr, slice, s, r, out, ct_begin,

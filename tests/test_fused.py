@@ -84,6 +84,8 @@ def _idx_cases():
                                                   dtype="f32", with_ranks=True)
     yield "fp32_two_launches", random_problem(rng, T=2100, D=64, out_sizes=(32,), r_max=8, S=5,
                                               dtype="f32", bad_idx_frac=0.1)
+    yield "fp32_one_launch_strided", random_problem(rng, T=150, D=200, out_sizes=(64, 36), r_max=12, S=7,
+                                                    dtype="f32", with_ranks=True, ldx=208, ldy=112)
     # two launches after the build kernel: every slot count, mostly gather
     # groups, a long contraction (K parts with atomics), no adapter at all
     yield "two_launches_S1024", random_problem(rng, T=5000, D=128, out_sizes=(64,), r_max=16, S=1024,

@@ -120,6 +120,15 @@ def edge_problems():
                        with_ranks=True)
     p.ranks[:] = [0, 3, 8]
     yield "rank_zero", p, "auto"
+    for mode in ("auto", "bgmv", "sgmv"):
+        # fp32 rows of r_max = 12 (a multiple of 4, not of 8): v rows end
+        # halfway through the kernels' 8-float pieces; long and short segments,
+        # the last token of the last slice on a slot of full rank
+        idx = np.repeat(np.arange(4, dtype=np.int32), [70, 9, 40, 31])
+        p = random_problem(rng, T=idx.size, D=72, out_sizes=(24, 40), r_max=12, S=4, dtype="f32",
+                           idx=idx, with_ranks=True)
+        p.ranks[:] = [5, 12, 8, 12]
+        yield f"rmax12_f32_{mode}", p, mode
 
 
 @pytest.mark.parametrize("case", list(edge_problems()), ids=lambda c: c[0])
