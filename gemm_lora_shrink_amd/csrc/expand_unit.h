@@ -79,13 +79,13 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const VSrc& vs
   const Elem* yzero = reinterpret_cast<const Elem*>(g_zero16);
   Elem* ybase = reinterpret_cast<Elem*>(p.y) + p.out_off[slice] + yc;
 
-  // y pieces and B rows of column tile ct (zeros past ct_end: the last
-  // prefetch issues only loads of the zero constant)
+  // B rows and y pieces of column tile ct (zeros past ct_end: the last
+  // prefetch issues only loads of the zero constant).  B first: loads complete
+  // in order, so the products, which need only B (mostly from L2), start
+  // while y is still on its way from HBM.
   auto load_tile = [&](int ct, u32x4 (&yd)[2], u32x4 (&bd)[4][2]) {
     const int jw = ct * kExpandColsPerWG + wave * kExpandColsPerWave;
     const bool ycol_ok = ct < ct_end && jw + yc < out;  // out is a multiple of 8
-    yd[0] = ld16_or0_nt(ycol_ok && ytok0 >= 0 ? ybase + jw + (int64_t)ytok0 * p.ldy : yzero, ycol_ok && ytok0 >= 0);
-    yd[1] = ld16_or0_nt(ycol_ok && ytok1 >= 0 ? ybase + jw + (int64_t)ytok1 * p.ldy : yzero, ycol_ok && ytok1 >= 0);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int row = jw + cb * 16 + n;
@@ -96,6 +96,8 @@ __device__ inline void expand_group_direct(const ExpandParams& p, const VSrc& vs
         bd[cb][ks] = ld16_or0(Bs + (ok ? (int64_t)row * ldb + k0 : 0), ok);
       }
     }
+    yd[0] = ld16_or0_nt(ycol_ok && ytok0 >= 0 ? ybase + jw + (int64_t)ytok0 * p.ldy : yzero, ycol_ok && ytok0 >= 0);
+    yd[1] = ld16_or0_nt(ycol_ok && ytok1 >= 0 ? ybase + jw + (int64_t)ytok1 * p.ldy : yzero, ycol_ok && ytok1 >= 0);
   };
   u32x4 ya[2], ba[4][2], yb[2], bb[4][2];
   load_tile(ct_begin, ya, ba);

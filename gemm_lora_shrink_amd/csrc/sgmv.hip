@@ -23,8 +23,10 @@ constexpr int kThreads = 256;
 // unit the workgroup reads the item's token list once and converts the item's
 // fp32 v rows once into the 16-bit hi/lo operands, kept in LDS for the four
 // waves.  Then, per column tile, wave w handles columns 64 w .. 64 w + 63:
-// it issues its y loads (lane-contiguous: eight lanes cover one token's 64
-// columns, 128 bytes) and its B-row loads first, runs the MFMAs per 16-token
+// it issues its B-row loads and then its y loads (lane-contiguous: eight lanes
+// cover one token's 64 columns, 128 bytes) -- loads complete in order, so the
+// products, which need only B, start while y is still on its way from HBM
+// (2 us of the fused-QKV prefill's expand) -- runs the MFMAs per 16-token
 // sub-block, transposes the fp32 result through a wave-private LDS block and
 // updates y with 16-byte accesses.  No workgroup barrier is needed inside a
 // unit.
@@ -107,8 +109,8 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
   };
   u32x4 yold[NSUB][2];
   u32x4 bop[8];
-  load_y(ct_begin, yold);
   load_b(ct_begin, bop);
+  load_y(ct_begin, yold);
 
   {
     float vv[16];
@@ -238,14 +240,14 @@ __device__ inline void expand_tile(const ExpandParams& p, int tok_v, int n_sub, 
     const int ct = ct_begin + i;
     if (ct >= ct_end) break;
     if (i + 1 < RUN) {
-      load_y(ct + 1, ynext);
       load_b(ct + 1, bnext);
+      load_y(ct + 1, ynext);
     }
     compute_tile(ct, yold, bop);
     if (i + 1 >= RUN || ct + 1 >= ct_end) break;
     if (i + 2 < RUN) {
-      load_y(ct + 2, yold);
       load_b(ct + 2, bop);
+      load_y(ct + 2, yold);
     }
     compute_tile(ct + 1, ynext, bnext);
   }
