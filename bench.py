@@ -577,10 +577,11 @@ def run_config(name, args, torch, glsa, dev, copy_gbs, headline):
                        frac_hbm=round(c["gbs"] / HBM_PEAK_GBS, 4), tflops=round(c["tflops"], 3),
                        in_step=c["in_step"])
                for k, c in calls.items()},
-        # the survey's per-config names for the figures above: gbps is the
-        # step's algorithmic rate, mfma_util the algorithmic MFMA share (the
-        # counter-measured one is in the committed MFMA summary), and the call
-        # times by kind (a one-launch call is shrink and expand together)
+        # the same figures under the per-config names of the measurement
+        # plan: gbps is the step's algorithmic rate, mfma_util the algorithmic
+        # MFMA share (the counter-measured one is in the committed MFMA
+        # summary), and the call times by kind (a one-launch call is shrink
+        # and expand together)
         gbps=round(step_gbs, 1),
         mfma_util=round(step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS_16, 5) if is16 else None,
         t_segments_us=round(sum(c["us"] for k, c in calls.items() if k == "segments"), 3),
@@ -650,7 +651,7 @@ def run_config(name, args, torch, glsa, dev, copy_gbs, headline):
     err_y = max(errs_y) if errs_y else 0.0
     err_v = max(errs_v)
     # err_y is the infinity-norm error of y relative to the oracle's largest
-    # |y| on the checked rows (the survey's err_inf)
+    # |y| on the checked rows (also reported as err_inf)
     out.update(err_y=float(f"{err_y:.3e}"), err_inf=float(f"{err_y:.3e}"), err_v=float(f"{err_v:.3e}"),
                frac_attainable=out["dominant"]["frac_attainable"], y_tol=Y_TOL[wl.dtype], v_tol=V_TOL,
                checked_rows=int(len(rows)), meta_bitexact=meta_ok, workspace_errors=int(gave_up))
